@@ -1,0 +1,20 @@
+"""CPU oracle for sink attention (float64, NumPy).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this package.  The HIP library's product path never imports it,
+and it imports nothing from the HIP package.
+"""
+from .sink_attention import (  # noqa: F401
+    NEG_INF,
+    attend,
+    causal_allowed,
+    chunk_size,
+    chunk_state,
+    decode,
+    decode_split,
+    merge,
+    online_row,
+    prefill,
+    prefill_at,
+    sink_softmax,
+)

@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+One step = one split-KV decode (sinkattn_decode_split + sinkattn_decode_merge) of the decode
+workload: 8 sequences x 8192 cached tokens, 64 query heads over 8 KV heads, head_dim 64, bf16,
+8 chunks of 1024 keys. ``value`` is algorithmic KV bytes per second (the K and V rows actually
+read plus q, out and sinks), with inputs resident in HBM. Decode inputs rotate over enough copies
+(> 512 MB in all) that the 256 MB Infinity Cache cannot serve a step from the previous one.
+
+The same JSON line also carries:
+* ``roofline`` for the dominant kernel (the split kernel), timed alone with events on the stream
+  it runs on, against the 8 TB/s HBM peak; ``traffic`` from the committed rocprofv3 FETCH_SIZE /
+  WRITE_SIZE summary when it was taken on the current kernel source, else null;
+* ``prefill``: causal prefill of one 8192-token sequence (64/8 heads, bf16), TFLOP/s over the
+  allowed causal pairs (4 * D per pair) against the 2.5 PFLOP/s dense bf16 MFMA peak;
+* ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of bf16 MFMA peak)"
+ROTATE_BYTES = 512 * 2**20
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_b8_len8192_pmc.txt")
+SPLIT_SOURCE = os.path.join(ROOT, "gqa_learned_softmax_amd", "csrc", "decode_split.hip")
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _source_hash(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(kernel_hash):
+    """(fetch + write) bytes per split launch from the committed PMC summary, if it matches."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_hash:
+        return None
+    return float(t.group(1))
+
+
+def _time_loop(fn, iters, torch):
+    """Average ms per call of ``fn(i)`` over ``iters`` back-to-back calls on the current stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(iters):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(case, kv_bytes):
+    """The oracle, as it stands, on the decode workload; repeated until >= 10 s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    q = case.q.double().numpy()
+    sinks = case.sinks.double().numpy()
+    ks = [case.k[b:b + 1, :int(n)].float().numpy() for b, n in enumerate(case.seqlens_k.tolist())]
+    vs = [case.v[b:b + 1, :int(n)].float().numpy() for b, n in enumerate(case.seqlens_k.tolist())]
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            for b, n in enumerate(case.seqlens_k.tolist()):
+                oracle.decode(q[b:b + 1], ks[b], vs[b], sinks, [int(n)], case.scale)
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= 10.0:
+                break
+    _ = np  # the oracle is NumPy float64
+    return {
+        "value": round(reps * kv_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole decode workload (8 seqs x 8192 keys, 64/8 heads) repeated {reps}x "
+                  f"in {elapsed:.1f} s, float64 NumPy, 1 BLAS thread",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the hot path here is a "
+              "single-GPU kernel library; no multi-GPU configuration exists.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gqa_learned_softmax_amd as sa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- decode workload (value)
+    _log("generating decode workload (8 x 8192, 64/8 heads, bf16)")
+    w = workloads.make(2)
+    case = w.decode
+    kv_bytes = workloads.decode_kv_bytes(case)
+    batch, hq, dim = case.q.shape
+    chunks = case.num_chunks
+    io_bytes = case.q.numel() * 2 + batch * hq * dim * 2 + case.sinks.numel() * 4
+    step_bytes = kv_bytes + io_bytes
+    split_bytes = kv_bytes + case.q.numel() * 2 + case.sinks.numel() * 4
+
+    set_bytes = case.k.numel() * 2 * 2
+    n_sets = max(2, -(-ROTATE_BYTES // set_bytes) + 1)
+    k0, v0 = case.k.to(dev), case.v.to(dev)
+    ks = [k0] + [k0.clone() for _ in range(n_sets - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n_sets - 1)]
+    q = case.q.to(dev)
+    sinks = case.sinks.to(dev)
+    seqlens = case.seqlens_k.to(dev)
+    po = torch.empty((batch, hq, chunks, dim), dtype=torch.float32, device=dev)
+    pm = torch.empty((batch, hq, chunks), dtype=torch.float32, device=dev)
+    pd = torch.empty((batch, hq, chunks), dtype=torch.float32, device=dev)
+    out = torch.empty((batch, hq, dim), dtype=torch.bfloat16, device=dev)
+
+    def split(i):
+        sa.decode_split(q, ks[i % n_sets], vs[i % n_sets], sinks, seqlens, chunks, case.scale, po, pm, pd)
+
+    def merge(i):
+        sa.decode_merge(po, pm, pd, out=out)
+
+    def step(i):
+        split(i)
+        merge(i)
+
+    def step_hot(i):
+        sa.decode_split(q, k0, v0, sinks, seqlens, chunks, case.scale, po, pm, pd)
+        merge(i)
+
+    _log(f"decode: {n_sets} rotating K/V sets of {set_bytes / 2**20:.0f} MiB; warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    t0 = time.perf_counter()
+    ms_step = _time_loop(step, args.steps, torch)
+    wall = time.perf_counter() - t0
+    _log(f"decode step {ms_step * 1e3:.2f} us ({wall:.3f} s wall for {args.steps} steps)")
+    ms_split = _time_loop(split, max(args.steps, 50), torch)
+    ms_merge = _time_loop(merge, max(args.steps, 50), torch)
+    ms_hot = _time_loop(step_hot, max(args.steps, 50), torch)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    split_gbs = split_bytes / (ms_split * 1e-3) / 1e9
+    _log(f"split {ms_split * 1e3:.2f} us ({split_gbs:.0f} GB/s), merge {ms_merge * 1e3:.2f} us, "
+         f"hot step {ms_hot * 1e3:.2f} us")
+
+    traffic = _traffic_from_profile(_source_hash(SPLIT_SOURCE))
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_b8_hq64_hkv8_d64_len8192_chunks8",
+            "batch": batch, "kv_len": 8192, "num_q_heads": hq, "num_kv_heads": case.k.shape[2],
+            "head_dim": dim, "num_chunks": chunks, "step": "decode_split + decode_merge",
+            "rotating_kv_sets": n_sets, "algorithmic_bytes_per_step": step_bytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_split_bf16",
+            "achieved": round(split_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": split_bytes,
+            "avg_launch_us": round(ms_split * 1e3, 3),
+        },
+        "decode_detail": {
+            "split_us": round(ms_split * 1e3, 3), "merge_us": round(ms_merge * 1e3, 3),
+            "step_us_rotated": round(ms_step * 1e3, 3), "step_us_hot": round(ms_hot * 1e3, 3),
+            "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        },
+    }
+    del ks, vs, k0, v0
+
+    # ---------------------------------------------------------------- prefill (second half of metric)
+    if not args.no_prefill:
+        _log("generating prefill workload (1 x 8192 causal, 64/8 heads, bf16)")
+        pre = workloads.make(3).prefill
+        pairs = workloads.prefill_causal_pairs(pre)
+        flops = 4.0 * dim * pre.q.shape[1] * pairs
+        pq, pk, pv = pre.q.to(dev), pre.k.to(dev), pre.v.to(dev)
+        ps, pcq, pck = pre.sinks.to(dev), pre.cu_seqlens_q.to(dev), pre.cu_seqlens_k.to(dev)
+        pout = torch.empty_like(pq)
+
+        def prefill(i):
+            sa.prefill(pq, pk, pv, ps, pcq, pck, pre.scale, True, out=pout)
+
+        for i in range(max(2, args.warmup // 2)):
+            prefill(i)
+        ms_pre = _time_loop(prefill, max(5, args.steps // 2), torch)
+        tflops = flops / (ms_pre * 1e-3) / 1e12
+        _log(f"prefill {ms_pre * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+        result["prefill"] = {
+            "workload": "prefill_b1_s8192_hq64_hkv8_d64_causal",
+            "ms_per_call": round(ms_pre, 4),
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "kernel": "prefill_bf16", "achieved": round(tflops, 2),
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flop_per_launch": flops},
+        }
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle on the decode workload (~10 s)")
+        result["cpu_baseline"] = cpu_baseline(case, step_bytes)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,75 @@
+"""Sink attention for AMD MI355X: Python face of the libsinkattn C ABI (include/sinkattn.h).
+
+Grouped-query attention whose softmax carries one learned logit per query head (the "sink") that
+adds to the denominator and has no value vector, as described in the blog post "GPT-OSS on Day 0"
+(Perplexity), section "Kernels for GPT-OSS", subsection "Sink attention".
+
+Each function marshals torch tensors into descriptors and calls the library on the current HIP
+stream. Allocation of outputs (when not given) is the only other thing done here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import SinkAttnError  # noqa: F401
+
+__all__ = ["prefill", "decode_split", "decode_merge", "decode", "SinkAttnError", "version"]
+
+
+def version() -> int:
+    return _lib.lib.sinkattn_version()
+
+
+def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal=True, out=None,
+            out_dtype=None):
+    """``sinkattn_prefill``: q [Tq, Hq, D], k/v [Tk, Hkv, D], sinks [Hq] f32, cu_seqlens [B+1] i32."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, out)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, out)]
+    _lib.check(_lib.lib.sinkattn_prefill(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        _lib.ref(d[5]), float(scale), 1 if causal else 0, _lib.ref(d[6]), _lib.stream_handle(dev)))
+    return out
+
+
+def decode_split(q, k, v, sinks, seqlens_k, num_chunks, scale, partial_o=None, partial_m=None,
+                 partial_d=None):
+    """``sinkattn_decode_split``: returns (partial_o [B,Hq,C,D], partial_m [B,Hq,C], partial_d)."""
+    batch, hq, dim = q.shape
+    if partial_o is None:
+        partial_o = torch.empty((batch, hq, num_chunks, dim), dtype=torch.float32, device=q.device)
+    if partial_m is None:
+        partial_m = torch.empty((batch, hq, num_chunks), dtype=torch.float32, device=q.device)
+    if partial_d is None:
+        partial_d = torch.empty((batch, hq, num_chunks), dtype=torch.float32, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, seqlens_k, partial_o, partial_m, partial_d)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k, partial_o, partial_m, partial_d)]
+    _lib.check(_lib.lib.sinkattn_decode_split(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        int(num_chunks), float(scale), _lib.ref(d[5]), _lib.ref(d[6]), _lib.ref(d[7]),
+        _lib.stream_handle(dev)))
+    return partial_o, partial_m, partial_d
+
+
+def decode_merge(partial_o, partial_m, partial_d, out=None, lse=None, out_dtype=torch.bfloat16,
+                 return_lse=False):
+    """``sinkattn_decode_merge``: out [B, Hq, D] (and lse [B, Hq] f32 when requested)."""
+    batch, hq, chunks, dim = partial_o.shape
+    if out is None:
+        out = torch.empty((batch, hq, dim), dtype=out_dtype, device=partial_o.device)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=partial_o.device)
+    dev = _lib.require_device(partial_o, partial_m, partial_d, out, lse)
+    d = [_lib.describe(t) for t in (partial_o, partial_m, partial_d, out, lse)]
+    _lib.check(_lib.lib.sinkattn_decode_merge(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), int(chunks), _lib.ref(d[3]),
+        _lib.ref(d[4]), _lib.stream_handle(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode(q, k, v, sinks, seqlens_k, num_chunks, scale, out=None, return_lse=False):
+    """Split then merge on the current stream (partials allocated with torch)."""
+    po, pm, pd = decode_split(q, k, v, sinks, seqlens_k, num_chunks, scale)
+    return decode_merge(po, pm, pd, out=out, out_dtype=q.dtype, return_lse=return_lse)

@@ -1,0 +1,490 @@
+// C ABI of libsinkattn: host-side validation and launch.
+//
+// Every check that needs no device access runs here, before any HIP call, so that a rejected
+// call launches nothing and writes nothing. The launchers in the kernel files only size grids.
+
+#include "sinkattn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sinkattn_status fail(sinkattn_status status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+#define SA_TRY(expr)                              \
+    do {                                          \
+        sinkattn_status _s = (expr);              \
+        if (_s != SINKATTN_OK) return _s;         \
+    } while (0)
+
+int64_t elem_size(sinkattn_dtype dt) {
+    switch (dt) {
+        case SINKATTN_F32: return 4;
+        case SINKATTN_BF16: return 2;
+        case SINKATTN_I32: return 4;
+    }
+    return 0;
+}
+
+const char* dtype_name(sinkattn_dtype dt) {
+    switch (dt) {
+        case SINKATTN_F32: return "f32";
+        case SINKATTN_BF16: return "bf16";
+        case SINKATTN_I32: return "i32";
+    }
+    return "?";
+}
+
+// Descriptor sanity: non-null, known dtype, expected rank, non-negative extents and strides.
+sinkattn_status check_desc(const sinkattn_tensor* t, const char* name, int ndim) {
+    if (t == nullptr) return fail(SINKATTN_ERR_NULL, "%s: descriptor is NULL", name);
+    if (t->dtype != SINKATTN_F32 && t->dtype != SINKATTN_BF16 && t->dtype != SINKATTN_I32)
+        return fail(SINKATTN_ERR_DTYPE, "%s: unknown dtype code %d", name, (int)t->dtype);
+    if (t->ndim != ndim)
+        return fail(SINKATTN_ERR_SHAPE, "%s: rank %d, expected %d", name, t->ndim, ndim);
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] < 0) return fail(SINKATTN_ERR_SHAPE, "%s: negative extent", name);
+        if (t->stride[i] < 0) return fail(SINKATTN_ERR_LAYOUT, "%s: negative stride", name);
+    }
+    return SINKATTN_OK;
+}
+
+int64_t numel(const sinkattn_tensor* t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    return n;
+}
+
+sinkattn_status check_data(const sinkattn_tensor* t, const char* name) {
+    if (numel(t) > 0 && t->data == nullptr)
+        return fail(SINKATTN_ERR_NULL, "%s: data pointer is NULL", name);
+    return SINKATTN_OK;
+}
+
+sinkattn_status check_dtype(const sinkattn_tensor* t, const char* name, sinkattn_dtype want) {
+    if (t->dtype != want)
+        return fail(SINKATTN_ERR_DTYPE, "%s: dtype %s, expected %s", name, dtype_name(t->dtype),
+                    dtype_name(want));
+    return SINKATTN_OK;
+}
+
+// Vector-loadable rows: 16-byte aligned base, unit inner stride, outer strides multiples of
+// 16 bytes. Extent-1 dimensions are never stepped, so their strides are not constrained.
+sinkattn_status check_rows(const sinkattn_tensor* t, const char* name) {
+    const int64_t es = elem_size(t->dtype);
+    const int last = t->ndim - 1;
+    if (t->stride[last] != 1 && t->shape[last] > 1)
+        return fail(SINKATTN_ERR_LAYOUT, "%s: innermost stride must be 1", name);
+    if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+        return fail(SINKATTN_ERR_LAYOUT, "%s: data pointer not 16-byte aligned", name);
+    for (int i = 0; i < last; ++i)
+        if (t->shape[i] > 1 && (t->stride[i] * es) % 16 != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "%s: stride of dim %d is not a multiple of 16 bytes",
+                        name, i);
+    return SINKATTN_OK;
+}
+
+bool is_contiguous(const sinkattn_tensor* t) {
+    int64_t expect = 1;
+    for (int i = t->ndim - 1; i >= 0; --i) {
+        if (t->shape[i] > 1 && t->stride[i] != expect) return false;
+        expect *= t->shape[i];
+    }
+    return true;
+}
+
+sinkattn_status check_contiguous(const sinkattn_tensor* t, const char* name) {
+    if (!is_contiguous(t)) return fail(SINKATTN_ERR_LAYOUT, "%s: must be contiguous", name);
+    if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+        return fail(SINKATTN_ERR_LAYOUT, "%s: data pointer not 16-byte aligned", name);
+    return SINKATTN_OK;
+}
+
+// Writes to an output must not collide: sorted by stride, every dimension must step past the
+// whole extent of the smaller ones.
+sinkattn_status check_no_self_overlap(const sinkattn_tensor* t, const char* name) {
+    int idx[4];
+    int n = 0;
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->shape[i] > 1) idx[n++] = i;
+    for (int a = 1; a < n; ++a)
+        for (int b = a; b > 0 && t->stride[idx[b]] < t->stride[idx[b - 1]]; --b) {
+            int tmp = idx[b];
+            idx[b] = idx[b - 1];
+            idx[b - 1] = tmp;
+        }
+    int64_t span = 1;
+    for (int a = 0; a < n; ++a) {
+        if (t->stride[idx[a]] < span)
+            return fail(SINKATTN_ERR_LAYOUT, "%s: strides make elements overlap", name);
+        span = t->stride[idx[a]] * t->shape[idx[a]];
+    }
+    return SINKATTN_OK;
+}
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi)
+};
+
+Span byte_span(const sinkattn_tensor* t) {
+    Span s;
+    if (t == nullptr || t->data == nullptr || numel(t) == 0) return s;
+    int64_t last = 0;
+    for (int i = 0; i < t->ndim; ++i) last += (t->shape[i] - 1) * t->stride[i];
+    s.lo = reinterpret_cast<uintptr_t>(t->data);
+    s.hi = s.lo + static_cast<uintptr_t>((last + 1) * elem_size(t->dtype));
+    return s;
+}
+
+sinkattn_status check_disjoint(const sinkattn_tensor* out, const char* oname,
+                               const sinkattn_tensor* in, const char* iname) {
+    Span a = byte_span(out), b = byte_span(in);
+    if (a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi)
+        return fail(SINKATTN_ERR_LAYOUT, "%s overlaps %s", oname, iname);
+    return SINKATTN_OK;
+}
+
+sinkattn_status check_scale(float scale) {
+    if (!std::isfinite(scale) || !(scale > 0.0f))
+        return fail(SINKATTN_ERR_SHAPE, "scale must be finite and > 0 (got %g)", (double)scale);
+    return SINKATTN_OK;
+}
+
+sinkattn_status check_vec(const sinkattn_tensor* t, const char* name, sinkattn_dtype dt,
+                          int64_t len) {
+    SA_TRY(check_desc(t, name, 1));
+    SA_TRY(check_dtype(t, name, dt));
+    if (t->shape[0] != len)
+        return fail(SINKATTN_ERR_SHAPE, "%s: length %lld, expected %lld", name,
+                    (long long)t->shape[0], (long long)len);
+    if (t->shape[0] > 1 && t->stride[0] != 1)
+        return fail(SINKATTN_ERR_LAYOUT, "%s: must be contiguous", name);
+    if (reinterpret_cast<uintptr_t>(t->data) % 4 != 0)
+        return fail(SINKATTN_ERR_LAYOUT, "%s: data pointer not 4-byte aligned", name);
+    return check_data(t, name);
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+sinkattn_status launched(hipError_t err) {
+    if (err != hipSuccess)
+        return fail(SINKATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
+    return SINKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                 const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                 const sinkattn_tensor* cu_seqlens_q,
+                                 const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
+                                 const sinkattn_tensor* out, void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(q, "q", 3));
+    SA_TRY(check_desc(k, "k", 3));
+    SA_TRY(check_desc(v, "v", 3));
+    SA_TRY(check_desc(out, "out", 3));
+    SA_TRY(check_desc(cu_seqlens_q, "cu_seqlens_q", 1));
+    SA_TRY(check_desc(cu_seqlens_k, "cu_seqlens_k", 1));
+
+    if (q->dtype != SINKATTN_BF16 && q->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "q: dtype must be bf16 or f32");
+    SA_TRY(check_dtype(k, "k", q->dtype));
+    SA_TRY(check_dtype(v, "v", q->dtype));
+    if (q->dtype == SINKATTN_F32) SA_TRY(check_dtype(out, "out", SINKATTN_F32));
+    else if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
+
+    const int64_t tq = q->shape[0], hq = q->shape[1], dim = q->shape[2];
+    const int64_t tk = k->shape[0], hkv = k->shape[1];
+    for (int i = 0; i < 3; ++i)
+        if (v->shape[i] != k->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, "v: shape differs from k");
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, "out: shape differs from q");
+    if (k->shape[2] != dim) return fail(SINKATTN_ERR_SHAPE, "k: head_dim differs from q");
+    if (hkv <= 0 || hq <= 0 || hq % hkv != 0)
+        return fail(SINKATTN_ERR_SHAPE, "query heads (%lld) must be a positive multiple of KV heads (%lld)",
+                    (long long)hq, (long long)hkv);
+    if (cu_seqlens_q->shape[0] < 1 || cu_seqlens_k->shape[0] != cu_seqlens_q->shape[0])
+        return fail(SINKATTN_ERR_SHAPE, "cu_seqlens_q/k must both have B+1 >= 1 entries");
+    const int64_t num_seqs = cu_seqlens_q->shape[0] - 1;
+    SA_TRY(check_vec(cu_seqlens_q, "cu_seqlens_q", SINKATTN_I32, num_seqs + 1));
+    SA_TRY(check_vec(cu_seqlens_k, "cu_seqlens_k", SINKATTN_I32, num_seqs + 1));
+    SA_TRY(check_vec(sinks, "sinks", SINKATTN_F32, hq));
+    SA_TRY(check_scale(scale));
+    if (dim != sinkattn::kHeadDim)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (only 64)", (long long)dim);
+    const int64_t group = hq / hkv;
+    if (!is_pow2(group) || group > 128)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "group size %lld not supported (powers of two up to 128)",
+                    (long long)group);
+    if (tq >= (int64_t(1) << 31) || tk >= (int64_t(1) << 31) || num_seqs >= (int64_t(1) << 24))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "token or sequence count too large");
+
+    SA_TRY(check_data(q, "q"));
+    SA_TRY(check_data(k, "k"));
+    SA_TRY(check_data(v, "v"));
+    SA_TRY(check_data(out, "out"));
+    SA_TRY(check_rows(q, "q"));
+    SA_TRY(check_rows(k, "k"));
+    SA_TRY(check_rows(v, "v"));
+    SA_TRY(check_rows(out, "out"));
+    SA_TRY(check_no_self_overlap(out, "out"));
+    SA_TRY(check_disjoint(out, "out", q, "q"));
+    SA_TRY(check_disjoint(out, "out", k, "k"));
+    SA_TRY(check_disjoint(out, "out", v, "v"));
+    SA_TRY(check_disjoint(out, "out", sinks, "sinks"));
+    SA_TRY(check_disjoint(out, "out", cu_seqlens_q, "cu_seqlens_q"));
+    SA_TRY(check_disjoint(out, "out", cu_seqlens_k, "cu_seqlens_k"));
+
+    if (tq == 0 || num_seqs == 0) return SINKATTN_OK;
+
+    sinkattn::PrefillParams p{};
+    p.q = q->data;
+    p.k = k->data;
+    p.v = v->data;
+    p.sinks = static_cast<const float*>(sinks->data);
+    p.cu_seqlens_q = static_cast<const int32_t*>(cu_seqlens_q->data);
+    p.cu_seqlens_k = static_cast<const int32_t*>(cu_seqlens_k->data);
+    p.out = out->data;
+    p.q_stride_tok = q->stride[0];
+    p.q_stride_head = q->stride[1];
+    p.k_stride_tok = k->stride[0];
+    p.k_stride_head = k->stride[1];
+    p.v_stride_tok = v->stride[0];
+    p.v_stride_head = v->stride[1];
+    p.o_stride_tok = out->stride[0];
+    p.o_stride_head = out->stride[1];
+    p.total_q = tq;
+    p.total_k = tk;
+    p.num_seqs = static_cast<int32_t>(num_seqs);
+    p.num_q_heads = static_cast<int32_t>(hq);
+    p.num_kv_heads = static_cast<int32_t>(hkv);
+    p.scale = scale;
+    p.causal = causal ? 1 : 0;
+    p.out_is_bf16 = out->dtype == SINKATTN_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_prefill_bf16(p, s)
+                                              : sinkattn::launch_prefill_f32(p, s));
+}
+
+sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                      const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                      const sinkattn_tensor* seqlens_k, int num_chunks,
+                                      float scale, const sinkattn_tensor* partial_o,
+                                      const sinkattn_tensor* partial_m,
+                                      const sinkattn_tensor* partial_d, void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(q, "q", 3));
+    SA_TRY(check_desc(k, "k", 4));
+    SA_TRY(check_desc(v, "v", 4));
+    SA_TRY(check_desc(partial_o, "partial_o", 4));
+    SA_TRY(check_desc(partial_m, "partial_m", 3));
+    SA_TRY(check_desc(partial_d, "partial_d", 3));
+
+    if (q->dtype != SINKATTN_BF16 && q->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "q: dtype must be bf16 or f32");
+    SA_TRY(check_dtype(k, "k", q->dtype));
+    SA_TRY(check_dtype(v, "v", q->dtype));
+    SA_TRY(check_dtype(partial_o, "partial_o", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_m, "partial_m", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_d, "partial_d", SINKATTN_F32));
+
+    const int64_t batch = q->shape[0], hq = q->shape[1], dim = q->shape[2];
+    const int64_t cap = k->shape[1], hkv = k->shape[2];
+    for (int i = 0; i < 4; ++i)
+        if (v->shape[i] != k->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, "v: shape differs from k");
+    if (k->shape[0] != batch) return fail(SINKATTN_ERR_SHAPE, "k: batch differs from q");
+    if (k->shape[3] != dim) return fail(SINKATTN_ERR_SHAPE, "k: head_dim differs from q");
+    if (hkv <= 0 || hq <= 0 || hq % hkv != 0)
+        return fail(SINKATTN_ERR_SHAPE, "query heads (%lld) must be a positive multiple of KV heads (%lld)",
+                    (long long)hq, (long long)hkv);
+    if (num_chunks < 1) return fail(SINKATTN_ERR_SHAPE, "num_chunks must be >= 1 (got %d)", num_chunks);
+    const int64_t want_o[4] = {batch, hq, num_chunks, dim};
+    for (int i = 0; i < 4; ++i)
+        if (partial_o->shape[i] != want_o[i])
+            return fail(SINKATTN_ERR_SHAPE, "partial_o: expected [B, Hq, num_chunks, D]");
+    for (int i = 0; i < 3; ++i)
+        if (partial_m->shape[i] != want_o[i] || partial_d->shape[i] != want_o[i])
+            return fail(SINKATTN_ERR_SHAPE, "partial_m/partial_d: expected [B, Hq, num_chunks]");
+    SA_TRY(check_vec(seqlens_k, "seqlens_k", SINKATTN_I32, batch));
+    SA_TRY(check_vec(sinks, "sinks", SINKATTN_F32, hq));
+    SA_TRY(check_scale(scale));
+    if (dim != sinkattn::kHeadDim)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (only 64)", (long long)dim);
+    const int64_t group = hq / hkv;
+    if (!is_pow2(group) || group > 16)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "group size %lld not supported (1, 2, 4, 8 or 16)",
+                    (long long)group);
+    if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+
+    SA_TRY(check_data(q, "q"));
+    SA_TRY(check_data(k, "k"));
+    SA_TRY(check_data(v, "v"));
+    SA_TRY(check_data(partial_o, "partial_o"));
+    SA_TRY(check_data(partial_m, "partial_m"));
+    SA_TRY(check_data(partial_d, "partial_d"));
+    SA_TRY(check_rows(q, "q"));
+    SA_TRY(check_rows(k, "k"));
+    SA_TRY(check_rows(v, "v"));
+    SA_TRY(check_contiguous(partial_o, "partial_o"));
+    SA_TRY(check_contiguous(partial_m, "partial_m"));
+    SA_TRY(check_contiguous(partial_d, "partial_d"));
+    const sinkattn_tensor* outs[3] = {partial_o, partial_m, partial_d};
+    const char* onames[3] = {"partial_o", "partial_m", "partial_d"};
+    const sinkattn_tensor* ins[5] = {q, k, v, sinks, seqlens_k};
+    const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 5; ++b) SA_TRY(check_disjoint(outs[a], onames[a], ins[b], inames[b]));
+        for (int b = a + 1; b < 3; ++b) SA_TRY(check_disjoint(outs[a], onames[a], outs[b], onames[b]));
+    }
+
+    if (batch == 0) return SINKATTN_OK;
+
+    sinkattn::DecodeSplitParams p{};
+    p.q = q->data;
+    p.k = k->data;
+    p.v = v->data;
+    p.sinks = static_cast<const float*>(sinks->data);
+    p.seqlens_k = static_cast<const int32_t*>(seqlens_k->data);
+    p.partial_o = static_cast<float*>(partial_o->data);
+    p.partial_m = static_cast<float*>(partial_m->data);
+    p.partial_d = static_cast<float*>(partial_d->data);
+    p.q_stride_b = q->stride[0];
+    p.q_stride_head = q->stride[1];
+    p.k_stride_b = k->stride[0];
+    p.k_stride_tok = k->stride[1];
+    p.k_stride_head = k->stride[2];
+    p.v_stride_b = v->stride[0];
+    p.v_stride_tok = v->stride[1];
+    p.v_stride_head = v->stride[2];
+    p.capacity = cap;
+    p.chunk_size = (cap + num_chunks - 1) / num_chunks;
+    p.batch = static_cast<int32_t>(batch);
+    p.num_q_heads = static_cast<int32_t>(hq);
+    p.num_kv_heads = static_cast<int32_t>(hkv);
+    p.num_chunks = num_chunks;
+    p.scale = scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_decode_split_bf16(p, s)
+                                              : sinkattn::launch_decode_split_f32(p, s));
+}
+
+sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
+                                      const sinkattn_tensor* partial_m,
+                                      const sinkattn_tensor* partial_d, int num_chunks,
+                                      const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                      void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(partial_o, "partial_o", 4));
+    SA_TRY(check_desc(partial_m, "partial_m", 3));
+    SA_TRY(check_desc(partial_d, "partial_d", 3));
+    SA_TRY(check_desc(out, "out", 3));
+    if (lse != nullptr) SA_TRY(check_desc(lse, "lse", 2));
+    SA_TRY(check_dtype(partial_o, "partial_o", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_m, "partial_m", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_d, "partial_d", SINKATTN_F32));
+    if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
+    if (lse != nullptr) SA_TRY(check_dtype(lse, "lse", SINKATTN_F32));
+
+    const int64_t batch = partial_o->shape[0], hq = partial_o->shape[1];
+    const int64_t chunks = partial_o->shape[2], dim = partial_o->shape[3];
+    if (num_chunks < 1 || num_chunks != chunks)
+        return fail(SINKATTN_ERR_SHAPE, "num_chunks (%d) must equal the chunk extent of partial_o (%lld)",
+                    num_chunks, (long long)chunks);
+    for (int i = 0; i < 3; ++i)
+        if (partial_m->shape[i] != partial_o->shape[i] || partial_d->shape[i] != partial_o->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, "partial_m/partial_d: expected [B, Hq, num_chunks]");
+    if (out->shape[0] != batch || out->shape[1] != hq || out->shape[2] != dim)
+        return fail(SINKATTN_ERR_SHAPE, "out: expected [B, Hq, D]");
+    if (lse != nullptr && (lse->shape[0] != batch || lse->shape[1] != hq))
+        return fail(SINKATTN_ERR_SHAPE, "lse: expected [B, Hq]");
+    if (dim != sinkattn::kHeadDim)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (only 64)", (long long)dim);
+    if (batch * hq >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+
+    SA_TRY(check_data(partial_o, "partial_o"));
+    SA_TRY(check_data(partial_m, "partial_m"));
+    SA_TRY(check_data(partial_d, "partial_d"));
+    SA_TRY(check_data(out, "out"));
+    if (lse != nullptr) {
+        SA_TRY(check_data(lse, "lse"));
+        if (reinterpret_cast<uintptr_t>(lse->data) % 4 != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "lse: data pointer not 4-byte aligned");
+        if (lse->stride[1] != 1 && lse->shape[1] > 1)
+            return fail(SINKATTN_ERR_LAYOUT, "lse: innermost stride must be 1");
+        SA_TRY(check_no_self_overlap(lse, "lse"));
+    }
+    SA_TRY(check_contiguous(partial_o, "partial_o"));
+    SA_TRY(check_contiguous(partial_m, "partial_m"));
+    SA_TRY(check_contiguous(partial_d, "partial_d"));
+    SA_TRY(check_rows(out, "out"));
+    SA_TRY(check_no_self_overlap(out, "out"));
+    const sinkattn_tensor* ins[3] = {partial_o, partial_m, partial_d};
+    const char* inames[3] = {"partial_o", "partial_m", "partial_d"};
+    for (int b = 0; b < 3; ++b) {
+        SA_TRY(check_disjoint(out, "out", ins[b], inames[b]));
+        if (lse != nullptr) SA_TRY(check_disjoint(lse, "lse", ins[b], inames[b]));
+    }
+    if (lse != nullptr) SA_TRY(check_disjoint(out, "out", lse, "lse"));
+
+    if (batch == 0 || hq == 0) return SINKATTN_OK;
+
+    sinkattn::DecodeMergeParams p{};
+    p.partial_o = static_cast<const float*>(partial_o->data);
+    p.partial_m = static_cast<const float*>(partial_m->data);
+    p.partial_d = static_cast<const float*>(partial_d->data);
+    p.out = out->data;
+    p.lse = lse != nullptr ? static_cast<float*>(lse->data) : nullptr;
+    p.o_stride_b = out->stride[0];
+    p.o_stride_head = out->stride[1];
+    p.lse_stride_b = lse != nullptr ? lse->stride[0] : 0;
+    p.lse_stride_head = lse != nullptr ? lse->stride[1] : 0;
+    p.batch = static_cast<int32_t>(batch);
+    p.num_q_heads = static_cast<int32_t>(hq);
+    p.num_chunks = num_chunks;
+    p.out_is_bf16 = out->dtype == SINKATTN_BF16;
+    return launched(sinkattn::launch_decode_merge(p, static_cast<hipStream_t>(stream)));
+}
+
+const char* sinkattn_status_string(sinkattn_status status) {
+    switch (status) {
+        case SINKATTN_OK: return "ok";
+        case SINKATTN_ERR_NULL: return "null pointer";
+        case SINKATTN_ERR_DTYPE: return "unsupported or mismatched dtype";
+        case SINKATTN_ERR_SHAPE: return "inconsistent shape or bad argument";
+        case SINKATTN_ERR_LAYOUT: return "unsupported memory layout";
+        case SINKATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SINKATTN_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
+
+int sinkattn_version(void) { return SINKATTN_VERSION; }
+
+}  // extern "C"

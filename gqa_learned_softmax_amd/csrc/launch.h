@@ -1,0 +1,77 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernel files.
+// Everything here has already been validated by api.cpp; launchers only compute grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+constexpr int kHeadDim = 64;
+
+// Packed varlen prefill. Strides in elements; the innermost (head_dim) stride is 1.
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* sinks;
+    const int32_t* cu_seqlens_q;
+    const int32_t* cu_seqlens_k;
+    void* out;
+    int64_t q_stride_tok, q_stride_head;
+    int64_t k_stride_tok, k_stride_head;
+    int64_t v_stride_tok, v_stride_head;
+    int64_t o_stride_tok, o_stride_head;
+    int64_t total_q;     // Tq
+    int64_t total_k;     // Tk
+    int32_t num_seqs;    // B
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    float scale;
+    int32_t causal;
+    int32_t out_is_bf16;
+};
+
+// Split-KV decode. q [B, Hq, D]; k/v [B, Lcap, Hkv, D]; partials contiguous.
+struct DecodeSplitParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* sinks;
+    const int32_t* seqlens_k;
+    float* partial_o;
+    float* partial_m;
+    float* partial_d;
+    int64_t q_stride_b, q_stride_head;
+    int64_t k_stride_b, k_stride_tok, k_stride_head;
+    int64_t v_stride_b, v_stride_tok, v_stride_head;
+    int64_t capacity;    // Lcap
+    int64_t chunk_size;  // ceil(Lcap / C)
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_chunks;
+    float scale;
+};
+
+struct DecodeMergeParams {
+    const float* partial_o;
+    const float* partial_m;
+    const float* partial_d;
+    void* out;
+    float* lse;          // may be null
+    int64_t o_stride_b, o_stride_head;
+    int64_t lse_stride_b, lse_stride_head;
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_chunks;
+    int32_t out_is_bf16;
+};
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream);
+hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream);
+
+}  // namespace sinkattn

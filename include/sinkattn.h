@@ -1,0 +1,180 @@
+/*
+ * sinkattn.h - C ABI of libsinkattn: grouped-query attention with a learned per-head softmax sink,
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (blog post "GPT-OSS on Day 0", Perplexity, 2025; section "Kernels for GPT-OSS",
+ * subsection "Sink attention"): every query head h owns one learned scalar sink[h]. For a query
+ * row q the attention weights are the softmax over the scaled logits scale * <q, k_j> of the keys
+ * the row may see, extended by one extra logit equal to sink[h]. The sink column has no value
+ * vector: it only adds e^(sink[h]) to the softmax denominator, so
+ *
+ *     out = sum_j e^(s_j) v_j / ( e^(sink[h]) + sum_j e^(s_j) ),   s_j = scale * <q, k_j>.
+ *
+ * The kernels compute this with the online softmax described in the same subsection: a running
+ * maximum m and running scale d per row, with m started at the head's sink value and d at 1 (the
+ * sink's own term). When the KV sequence is split into chunks, the sink is folded into the first
+ * chunk only (chunk 0) and the chunks are combined by a log-sum-exp merge.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are passed as sinkattn_tensor descriptors: a device pointer, an element type, a rank
+ *    and per-dimension extents and strides (strides in elements). The innermost dimension must have
+ *    stride 1. Data pointers must be 16-byte aligned and every non-inner stride a multiple of
+ *    8 elements (bf16) or 4 elements (fp32), so rows can be moved with 128-bit loads.
+ *  - head_dim D must be 64. Hq must be a multiple of Hkv; query head h reads KV head h / (Hq/Hkv)
+ *    (contiguous groups).
+ *  - q, k, v (and out) are either all bf16 (the MFMA fast path) or all fp32 (the reference
+ *    variant). With bf16 inputs `out` may be bf16 or fp32. Softmax state and accumulation are fp32.
+ *  - The library allocates nothing, frees nothing, never synchronises the stream and never reads
+ *    device memory on the host. Every call is stateless and reentrant; work is enqueued on
+ *    `stream` (a hipStream_t; NULL means the default stream).
+ *  - Outputs must not overlap inputs (checked on the host from the descriptors).
+ *  - All checks that can be made on the host run before any launch. On any error nothing is
+ *    launched and nothing is written; the status says which class of error it was, and
+ *    sinkattn_last_error() returns a message for the calling thread. A launch the HIP runtime
+ *    rejects returns SINKATTN_ERR_LAUNCH. Faults inside kernels surface at the caller's next
+ *    synchronisation, like any HIP kernel.
+ *  - Device-side preconditions (documented, not checked, since checking them would need a device
+ *    read): cu_seqlens are non-decreasing, start at 0 and end at the token counts; seqlens_k[b] is
+ *    in [0, Lcap]. Kernels clamp indices so that a broken precondition cannot read or write out
+ *    of the tensors' bounds; the values computed are then unspecified.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SINKATTN_VERSION 1
+
+typedef enum {
+    SINKATTN_OK = 0,
+    SINKATTN_ERR_NULL = 1,        /* a required descriptor or data pointer is NULL */
+    SINKATTN_ERR_DTYPE = 2,       /* element type not allowed for this argument, or mismatched */
+    SINKATTN_ERR_SHAPE = 3,       /* wrong rank, inconsistent extents, bad scalar argument */
+    SINKATTN_ERR_LAYOUT = 4,      /* misaligned pointer, non-unit inner stride, bad stride, overlap */
+    SINKATTN_ERR_UNSUPPORTED = 5, /* well-formed but not implemented (e.g. head_dim != 64) */
+    SINKATTN_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+} sinkattn_status;
+
+typedef enum {
+    SINKATTN_F32 = 0,
+    SINKATTN_BF16 = 1,
+    SINKATTN_I32 = 2
+} sinkattn_dtype;
+
+/* A strided view of device memory. Only the first `ndim` entries of shape/stride are read. */
+typedef struct {
+    void* data;          /* device pointer (caller-owned) */
+    sinkattn_dtype dtype;
+    int32_t ndim;        /* 1..4 */
+    int64_t shape[4];    /* extents, >= 0 */
+    int64_t stride[4];   /* in elements */
+} sinkattn_tensor;
+
+/*
+ * sinkattn_prefill - causal (or full) varlen prefill over a packed batch of B sequences.
+ *
+ * Source: "GPT-OSS on Day 0", "Sink attention" subsection: the sink-attention formula, evaluated
+ * with the online softmax whose running max starts at the head's sink. One work-group walks every
+ * KV tile of its query rows, so the sink is folded once per row, before the first tile.
+ *
+ *   q            [Tq, Hq, D]   bf16 | fp32   packed queries of all sequences
+ *   k, v         [Tk, Hkv, D]  same dtype as q
+ *   sinks        [Hq]          fp32          learned sink logit per query head (finite or -inf;
+ *                                            it is NOT multiplied by `scale`)
+ *   cu_seqlens_q [B+1]         int32 device  prefix sums of query lengths (cu[0] = 0, cu[B] = Tq)
+ *   cu_seqlens_k [B+1]         int32 device  prefix sums of key lengths   (cu[B] = Tk)
+ *   scale        finite, > 0 (typically 1/sqrt(D))
+ *   causal       nonzero: query i of a sequence with Lq queries and Lk keys sees keys
+ *                j <= i + (Lk - Lq) (bottom-right aligned; with Lq = Lk the usual j <= i).
+ *                zero: every query sees every key of its sequence.
+ *   out          [Tq, Hq, D]   bf16 | fp32 (fp32 only if q is fp32)
+ *
+ * A row that sees no key returns 0 (all weight sits on the value-less sink; with sink = -inf the
+ * 0/0 row is defined as 0). Tq = 0 or B = 0 launches nothing and returns SINKATTN_OK.
+ * Supported group sizes Hq/Hkv: powers of two up to 64.
+ */
+sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                 const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                 const sinkattn_tensor* cu_seqlens_q,
+                                 const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
+                                 const sinkattn_tensor* out, void* stream);
+
+/*
+ * sinkattn_decode_split - one query token per sequence against a padded KV cache, split along the
+ * KV length into `num_chunks` chunks of cs = ceil(Lcap / num_chunks) keys.
+ *
+ * Source: "GPT-OSS on Day 0", "Sink attention" subsection: attention is parallelised over heads
+ * and over KV length, and the sink is counted in the first chunk only. Chunk c of sequence b
+ * covers keys [c*cs, min((c+1)*cs, seqlens_k[b])); chunk 0 always carries the sink, even when it
+ * holds no key. For every (b, query head h, chunk c) the call writes the chunk's softmax state:
+ *
+ *   partial_m[b,h,c] = m_c, the largest logit of the chunk (with the sink for c = 0), natural log;
+ *   partial_d[b,h,c] = d_c = sum over the chunk's terms of e^(term - m_c);
+ *   partial_o[b,h,c,:] = (sum_j e^(s_j - m_c) v_j) / d_c, the chunk's normalised output.
+ *
+ * An empty chunk c >= 1 writes m = -inf, d = 0, o = 0. Only (m_c + ln d_c) and o_c are
+ * determined by the mathematics; m_c may differ from the exact maximum by rounding.
+ *
+ *   q          [B, Hq, D]          bf16 | fp32
+ *   k, v       [B, Lcap, Hkv, D]   same dtype as q; rows at or past seqlens_k[b] are never read
+ *   sinks      [Hq]                fp32
+ *   seqlens_k  [B]                 int32 device, each in [0, Lcap]
+ *   num_chunks C >= 1
+ *   scale      finite, > 0
+ *   partial_o  [B, Hq, C, D] fp32, contiguous
+ *   partial_m, partial_d [B, Hq, C] fp32, contiguous
+ *
+ * Supported group sizes Hq/Hkv: 1, 2, 4, 8, 16. B = 0 launches nothing.
+ */
+sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                      const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                      const sinkattn_tensor* seqlens_k, int num_chunks,
+                                      float scale, const sinkattn_tensor* partial_o,
+                                      const sinkattn_tensor* partial_m,
+                                      const sinkattn_tensor* partial_d, void* stream);
+
+/*
+ * sinkattn_decode_merge - log-sum-exp merge of the chunk states written by sinkattn_decode_split.
+ *
+ * Source: the chunk combination that the "Sink attention" subsection's split along the KV length
+ * requires (the page describes the split and the first-chunk rule, not the combination; this is
+ * the standard log-sum-exp merge of softmax states). Per (b, h):
+ *
+ *   M = max_c m_c,  w_c = d_c e^(m_c - M) (0 when m_c = -inf),
+ *   out = sum_c w_c o_c / sum_c w_c,  lse = M + ln sum_c w_c.
+ *
+ * The sink is counted once because only chunk 0 carries it. If every chunk is empty and the sink
+ * is -inf, out = 0 and lse = -inf.
+ *
+ *   partial_o  [B, Hq, C, D] fp32, contiguous
+ *   partial_m, partial_d [B, Hq, C] fp32, contiguous
+ *   num_chunks C, must equal the chunk extent of the partials
+ *   out        [B, Hq, D] bf16 | fp32
+ *   lse        [B, Hq] fp32 or NULL (not written)
+ */
+sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
+                                      const sinkattn_tensor* partial_m,
+                                      const sinkattn_tensor* partial_d, int num_chunks,
+                                      const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                      void* stream);
+
+/* Short static description of a status code. Never NULL. */
+const char* sinkattn_status_string(sinkattn_status status);
+
+/* Detail of the last error reported on the calling thread ("" if none). Valid until the thread's
+ * next sinkattn call. */
+const char* sinkattn_last_error(void);
+
+/* SINKATTN_VERSION of the built library. */
+int sinkattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */

@@ -1,0 +1,236 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/sinkattn.h
+declares, and rejects every malformed call on the host, before any HIP call.
+
+Descriptors here carry fake (but aligned, disjoint) device addresses: validation never
+dereferences them, and every call below is rejected before a launch could happen. The only
+accepted calls are the empty ones (Tq = 0, B = 0), which launch nothing by contract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_learned_softmax_amd import _lib
+from gqa_learned_softmax_amd._lib import BF16, F32, I32, Tensor
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sinkattn.h")
+
+_next_addr = [1 << 40]
+
+
+def T(shape, dtype=BF16, strides=None, addr=None):
+    d = Tensor()
+    if addr is None:
+        addr = _next_addr[0]
+        _next_addr[0] += 1 << 32  # every tensor in its own 4 GiB window: no accidental overlap
+    d.data = addr
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(shape):
+            strides.insert(0, acc)
+            acc *= n
+    for i, (n, s) in enumerate(zip(shape, strides)):
+        d.shape[i] = n
+        d.stride[i] = s
+    return d
+
+
+def R(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def last_error():
+    return _lib.lib.sinkattn_last_error().decode()
+
+
+# ----------------------------------------------------------------------------- exports
+def test_every_declared_function_is_exported():
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:const\s+char\s*\*|sinkattn_status|int)\s+(sinkattn_\w+)\s*\(",
+                           text, flags=re.M))
+    assert {"sinkattn_prefill", "sinkattn_decode_split", "sinkattn_decode_merge"} <= names
+    for name in names:
+        assert hasattr(_lib.lib, name), name
+    assert names == set(_lib.EXPORTS)
+
+
+def test_version_and_status_strings():
+    text = open(HEADER).read()
+    version = int(re.search(r"#define SINKATTN_VERSION (\d+)", text).group(1))
+    assert _lib.lib.sinkattn_version() == version
+    for code in range(7):
+        s = _lib.lib.sinkattn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert _lib.lib.sinkattn_status_string(123).decode() == "unknown status"
+
+
+# ----------------------------------------------------------------------------- prefill
+def prefill_args(tq=16, hq=8, hkv=2, dim=64, b=1, dtype=BF16, out_dtype=None):
+    return dict(
+        q=T([tq, hq, dim], dtype), k=T([tq, hkv, dim], dtype), v=T([tq, hkv, dim], dtype),
+        sinks=T([hq], F32), cu_q=T([b + 1], I32), cu_k=T([b + 1], I32),
+        out=T([tq, hq, dim], out_dtype if out_dtype is not None else dtype), scale=0.125, causal=1)
+
+
+def call_prefill(a):
+    return _lib.lib.sinkattn_prefill(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]), R(a["cu_q"]),
+                                     R(a["cu_k"]), a["scale"], a["causal"], R(a["out"]), None)
+
+
+def test_prefill_empty_batch_is_ok_and_launches_nothing():
+    assert call_prefill(prefill_args(tq=0)) == _lib.OK
+    assert call_prefill(prefill_args(tq=0, b=0)) == _lib.OK
+
+
+def _mut(a, **kw):
+    a = dict(a)
+    a.update(kw)
+    return a
+
+
+PREFILL_CASES = [
+    ("q_null", lambda a: _mut(a, q=None), _lib.ERR_NULL),
+    ("out_null", lambda a: _mut(a, out=None), _lib.ERR_NULL),
+    ("sinks_null", lambda a: _mut(a, sinks=None), _lib.ERR_NULL),
+    ("q_data_null", lambda a: _mut(a, q=T([16, 8, 64], addr=0)), _lib.ERR_NULL),
+    ("k_dtype_mismatch", lambda a: _mut(a, k=T([16, 2, 64], F32)), _lib.ERR_DTYPE),
+    ("q_int", lambda a: _mut(a, q=T([16, 8, 64], I32)), _lib.ERR_DTYPE),
+    ("unknown_dtype", lambda a: _mut(a, v=T([16, 2, 64], 7)), _lib.ERR_DTYPE),
+    ("sinks_bf16", lambda a: _mut(a, sinks=T([8], BF16)), _lib.ERR_DTYPE),
+    ("cu_f32", lambda a: _mut(a, cu_q=T([2], F32)), _lib.ERR_DTYPE),
+    ("q_rank2", lambda a: _mut(a, q=T([16, 512])), _lib.ERR_SHAPE),
+    ("heads_not_multiple", lambda a: _mut(a, q=T([16, 6, 64]), out=T([16, 6, 64]), sinks=T([6], F32),
+                                          k=T([16, 4, 64]), v=T([16, 4, 64])), _lib.ERR_SHAPE),
+    ("out_shape", lambda a: _mut(a, out=T([16, 4, 64])), _lib.ERR_SHAPE),
+    ("v_shape", lambda a: _mut(a, v=T([15, 2, 64])), _lib.ERR_SHAPE),
+    ("k_dim", lambda a: _mut(a, k=T([16, 2, 32]), v=T([16, 2, 32])), _lib.ERR_SHAPE),
+    ("sinks_len", lambda a: _mut(a, sinks=T([7], F32)), _lib.ERR_SHAPE),
+    ("cu_len_mismatch", lambda a: _mut(a, cu_k=T([3], I32)), _lib.ERR_SHAPE),
+    ("cu_empty", lambda a: _mut(a, cu_q=T([0], I32), cu_k=T([0], I32)), _lib.ERR_SHAPE),
+    ("scale_zero", lambda a: _mut(a, scale=0.0), _lib.ERR_SHAPE),
+    ("scale_negative", lambda a: _mut(a, scale=-0.125), _lib.ERR_SHAPE),
+    ("scale_nan", lambda a: _mut(a, scale=float("nan")), _lib.ERR_SHAPE),
+    ("scale_inf", lambda a: _mut(a, scale=float("inf")), _lib.ERR_SHAPE),
+    ("head_dim_128", lambda a: prefill_args(dim=128), _lib.ERR_UNSUPPORTED),
+    ("group_3", lambda a: prefill_args(hq=6, hkv=2), _lib.ERR_UNSUPPORTED),
+    ("q_misaligned", lambda a: _mut(a, q=T([16, 8, 64], addr=(3 << 44) + 2)), _lib.ERR_LAYOUT),
+    ("q_inner_stride", lambda a: _mut(a, q=T([16, 8, 64], strides=[1024, 128, 2])), _lib.ERR_LAYOUT),
+    ("k_head_stride_odd", lambda a: _mut(a, k=T([16, 2, 64], strides=[136, 68, 1])), _lib.ERR_LAYOUT),
+    ("negative_stride", lambda a: _mut(a, v=T([16, 2, 64], strides=[-128, 64, 1])), _lib.ERR_LAYOUT),
+    ("cu_strided", lambda a: _mut(a, cu_q=T([2], I32, strides=[2])), _lib.ERR_LAYOUT),
+    ("out_self_overlap", lambda a: _mut(a, out=T([16, 8, 64], strides=[0, 64, 1])), _lib.ERR_LAYOUT),
+    ("out_aliases_q", lambda a: _mut(a, out=T([16, 8, 64], addr=a["q"].data)), _lib.ERR_LAYOUT),
+    ("out_overlaps_k", lambda a: _mut(a, out=T([16, 8, 64], addr=a["k"].data + 1024)), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_rejects(name, mutate, code):
+    status = call_prefill(mutate(prefill_args()))
+    assert status == code, (status, last_error())
+    assert last_error(), "an error must leave a message"
+
+
+def test_prefill_f32_inputs_need_f32_out():
+    assert call_prefill(prefill_args(dtype=F32, out_dtype=BF16)) == _lib.ERR_DTYPE
+    # bf16 inputs may write fp32 out: accepted (checked through an empty call)
+    assert call_prefill(prefill_args(tq=0, out_dtype=F32)) == _lib.OK
+
+
+# ----------------------------------------------------------------------------- decode_split
+def split_args(b=2, hq=8, hkv=1, cap=64, chunks=4, dim=64, dtype=BF16):
+    return dict(q=T([b, hq, dim], dtype), k=T([b, cap, hkv, dim], dtype), v=T([b, cap, hkv, dim], dtype),
+                sinks=T([hq], F32), seqlens=T([b], I32), chunks=chunks, scale=0.125,
+                po=T([b, hq, chunks, dim], F32), pm=T([b, hq, chunks], F32), pd=T([b, hq, chunks], F32))
+
+
+def call_split(a):
+    return _lib.lib.sinkattn_decode_split(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]), R(a["seqlens"]),
+                                          a["chunks"], a["scale"], R(a["po"]), R(a["pm"]), R(a["pd"]), None)
+
+
+def test_split_empty_batch_is_ok():
+    assert call_split(split_args(b=0)) == _lib.OK
+
+
+SPLIT_CASES = [
+    ("k_null", lambda a: _mut(a, k=None), _lib.ERR_NULL),
+    ("seqlens_null", lambda a: _mut(a, seqlens=None), _lib.ERR_NULL),
+    ("partial_bf16", lambda a: _mut(a, po=T([2, 8, 4, 64], BF16)), _lib.ERR_DTYPE),
+    ("seqlens_f32", lambda a: _mut(a, seqlens=T([2], F32)), _lib.ERR_DTYPE),
+    ("chunks_zero", lambda a: _mut(a, chunks=0), _lib.ERR_SHAPE),
+    ("chunks_negative", lambda a: _mut(a, chunks=-3), _lib.ERR_SHAPE),
+    ("partial_chunks_mismatch", lambda a: _mut(a, chunks=5), _lib.ERR_SHAPE),
+    ("k_batch", lambda a: _mut(a, k=T([3, 64, 1, 64]), v=T([3, 64, 1, 64])), _lib.ERR_SHAPE),
+    ("k_rank3", lambda a: _mut(a, k=T([2, 64, 64])), _lib.ERR_SHAPE),
+    ("seqlens_len", lambda a: _mut(a, seqlens=T([3], I32)), _lib.ERR_SHAPE),
+    ("pm_shape", lambda a: _mut(a, pm=T([2, 8, 3], F32)), _lib.ERR_SHAPE),
+    ("scale_zero", lambda a: _mut(a, scale=0.0), _lib.ERR_SHAPE),
+    ("group_32", lambda a: split_args(hq=32), _lib.ERR_UNSUPPORTED),
+    ("group_6", lambda a: split_args(hq=6), _lib.ERR_UNSUPPORTED),
+    ("head_dim_96", lambda a: split_args(dim=96), _lib.ERR_UNSUPPORTED),
+    ("partial_o_strided", lambda a: _mut(a, po=T([2, 8, 4, 64], F32, strides=[4096, 512, 128, 1])), _lib.ERR_LAYOUT),
+    ("k_misaligned", lambda a: _mut(a, k=T([2, 64, 1, 64], addr=(5 << 44) + 8)), _lib.ERR_LAYOUT),
+    ("partial_overlaps_k", lambda a: _mut(a, po=T([2, 8, 4, 64], F32, addr=a["k"].data)), _lib.ERR_LAYOUT),
+    ("pm_overlaps_pd", lambda a: _mut(a, pm=T([2, 8, 4], F32, addr=a["pd"].data + 16)), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_rejects(name, mutate, code):
+    status = call_split(mutate(split_args()))
+    assert status == code, (status, last_error())
+    assert last_error()
+
+
+# ----------------------------------------------------------------------------- decode_merge
+def merge_args(b=2, hq=8, chunks=4, dim=64, out_dtype=BF16, lse=True):
+    return dict(po=T([b, hq, chunks, dim], F32), pm=T([b, hq, chunks], F32), pd=T([b, hq, chunks], F32),
+                chunks=chunks, out=T([b, hq, dim], out_dtype), lse=T([b, hq], F32) if lse else None)
+
+
+def call_merge(a):
+    return _lib.lib.sinkattn_decode_merge(R(a["po"]), R(a["pm"]), R(a["pd"]), a["chunks"], R(a["out"]),
+                                          R(a["lse"]), None)
+
+
+def test_merge_empty_batch_is_ok():
+    assert call_merge(merge_args(b=0)) == _lib.OK
+    assert call_merge(merge_args(b=0, lse=False)) == _lib.OK
+
+
+MERGE_CASES = [
+    ("po_null", lambda a: _mut(a, po=None), _lib.ERR_NULL),
+    ("out_null", lambda a: _mut(a, out=None), _lib.ERR_NULL),
+    ("out_int", lambda a: _mut(a, out=T([2, 8, 64], I32)), _lib.ERR_DTYPE),
+    ("lse_bf16", lambda a: _mut(a, lse=T([2, 8], BF16)), _lib.ERR_DTYPE),
+    ("chunks_mismatch", lambda a: _mut(a, chunks=3), _lib.ERR_SHAPE),
+    ("chunks_zero", lambda a: _mut(a, chunks=0), _lib.ERR_SHAPE),
+    ("out_shape", lambda a: _mut(a, out=T([2, 4, 64])), _lib.ERR_SHAPE),
+    ("lse_shape", lambda a: _mut(a, lse=T([2, 4], F32)), _lib.ERR_SHAPE),
+    ("pd_shape", lambda a: _mut(a, pd=T([2, 8, 5], F32)), _lib.ERR_SHAPE),
+    ("head_dim_32", lambda a: merge_args(dim=32), _lib.ERR_UNSUPPORTED),
+    ("po_gapped", lambda a: _mut(a, po=T([2, 8, 4, 64], F32, strides=[4096, 512, 64, 1])), _lib.ERR_LAYOUT),
+    ("out_overlaps_po", lambda a: _mut(a, out=T([2, 8, 64], addr=a["po"].data)), _lib.ERR_LAYOUT),
+    ("lse_overlaps_out", lambda a: _mut(a, lse=T([2, 8], F32, addr=a["out"].data)), _lib.ERR_LAYOUT),
+    ("pm_noncontiguous", lambda a: _mut(a, pm=T([2, 8, 4], F32, strides=[64, 8, 2])), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", MERGE_CASES, ids=[c[0] for c in MERGE_CASES])
+def test_merge_rejects(name, mutate, code):
+    status = call_merge(mutate(merge_args()))
+    assert status == code, (status, last_error())
+    assert last_error()
+
+
+def test_error_message_is_cleared_by_next_call():
+    call_merge(_mut(merge_args(), chunks=0))
+    assert last_error()
+    assert call_merge(merge_args(b=0)) == _lib.OK
+    assert last_error() == ""

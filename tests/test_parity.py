@@ -1,0 +1,314 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the float64 CPU oracle.
+
+Both sides see the same seeded inputs (bf16 values upcast exactly for the oracle). Bars:
+* bf16 inputs, fp32 accumulation: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3 over
+  all compared output elements;
+* fp32 reference variant: ||gpu - oracle||_inf / ||oracle||_inf <= 1e-5.
+Small cases compare every output element; the full-size workloads compare every output where the
+oracle is cheap (decode) and sampled (token, head) rows otherwise (prefill).
+"""
+from __future__ import annotations
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 2e-3
+F32_REL = 1e-5
+
+
+def _sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_learned_softmax_amd as sa  # raises if the HIP library is missing
+
+    return sa
+
+
+def _np(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _np32(t):
+    """Exact float32 copy of a (bf16 or f32) CPU tensor, for large oracle inputs."""
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _seed(name):
+    return zlib.crc32(name.encode()) % 10_000
+
+
+def _dev(*ts):
+    return [t.cuda() for t in ts]
+
+
+def check_bf16(gpu, ref, label=""):
+    g = _np(gpu)
+    err = np.abs(g - ref)
+    assert np.all(np.isfinite(g)), f"{label}: non-finite output"
+    max_abs, mean_abs = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    print(f"{label}: max_abs={max_abs:.3e} mean_abs={mean_abs:.3e}", flush=True)
+    assert max_abs <= BF16_MAX_ABS, f"{label}: max_abs {max_abs}"
+    assert mean_abs <= BF16_MEAN_ABS, f"{label}: mean_abs {mean_abs}"
+
+
+def check_f32(gpu, ref, label=""):
+    g = _np(gpu)
+    scale = float(np.abs(ref).max(initial=0.0))
+    rel = float(np.abs(g - ref).max(initial=0.0)) / (scale if scale > 0 else 1.0)
+    print(f"{label}: normwise rel={rel:.3e}", flush=True)
+    assert rel <= F32_REL, f"{label}: rel {rel}"
+
+
+def run_prefill(sa, case, out_dtype=None):
+    q, k, v, sinks, cq, ck = _dev(case.q, case.k, case.v, case.sinks, case.cu_seqlens_q, case.cu_seqlens_k)
+    out = sa.prefill(q, k, v, sinks, cq, ck, case.scale, case.causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prefill(case):
+    return oracle.prefill(_np(case.q), _np(case.k), _np(case.v), _np(case.sinks),
+                          case.cu_seqlens_q.numpy(), case.cu_seqlens_k.numpy(), case.scale, case.causal)
+
+
+def oracle_decode(case):
+    """Oracle decode, one sequence at a time (bounds host memory for large caches)."""
+    outs, lses = [], []
+    for b in range(case.q.shape[0]):
+        n = int(case.seqlens_k[b])
+        o, l = oracle.decode(_np(case.q[b:b + 1]), _np32(case.k[b:b + 1, :n]), _np32(case.v[b:b + 1, :n]),
+                             _np(case.sinks), [n], case.scale)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def run_decode(sa, case, return_lse=True):
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    po, pm, pd = sa.decode_split(q, k, v, sinks, sl, case.num_chunks, case.scale)
+    out, lse = sa.decode_merge(po, pm, pd, out_dtype=q.dtype, return_lse=True)
+    torch.cuda.synchronize()
+    return po, pm, pd, out, lse
+
+
+def check_partials(po, pm, pd, case, checker, label):
+    """Split-level parity: o_c and the chunk log-mass m_c + ln d_c, per chunk."""
+    ro, rm, rd = oracle.decode_split(_np(case.q), _np32(case.k), _np32(case.v), _np(case.sinks),
+                                     case.seqlens_k.numpy(), case.num_chunks, case.scale)
+    checker(po, ro, f"{label} partial_o")
+    gm, gd = _np(pm), _np(pd)
+    with np.errstate(divide="ignore"):
+        g_mass = np.where(gd > 0, gm + np.log(np.where(gd > 0, gd, 1.0)), -np.inf)
+        r_mass = np.where(rd > 0, rm + np.log(np.where(rd > 0, rd, 1.0)), -np.inf)
+    assert np.array_equal(np.isneginf(g_mass), np.isneginf(r_mass)), f"{label}: empty-chunk pattern"
+    fin = np.isfinite(r_mass)
+    np.testing.assert_allclose(g_mass[fin], r_mass[fin], rtol=0, atol=1e-3 if checker is check_bf16 else 1e-5)
+    assert np.all(gd[~fin] == 0) and np.all(_np(po)[~fin] == 0)
+
+
+# ----------------------------------------------------------------------------- tiny fp32 (C1)
+def test_tiny_fp32_prefill_and_decode():
+    sa = _sa()
+    w = workloads.make(1)
+    out = run_prefill(sa, w.prefill)
+    ref, _ = oracle_prefill(w.prefill)
+    check_f32(out, ref, "tiny prefill f32")
+
+    for name, case in (("fresh", w.decode), ("last_row", w.extra["decode_last_row"])):
+        po, pm, pd, dout, lse = run_decode(sa, case)
+        check_partials(po, pm, pd, case, check_f32, f"tiny decode {name}")
+        rout, rlse = oracle_decode(case)
+        check_f32(dout, rout, f"tiny decode {name}")
+        np.testing.assert_allclose(_np(lse), rlse, rtol=1e-5)
+    # decode of the prefill's last row equals prefill row 127, on the GPU
+    check_f32(dout[0], _np(out)[127], "tiny decode == prefill last row")
+
+
+# ----------------------------------------------------------------------------- bf16 prefill, small
+PREFILL_SMALL = [
+    # (name, lens_q, lens_k, Hq, Hkv, causal, sink_range)
+    ("one_seq_ragged", [200], None, 64, 8, True, (-2, 2)),
+    ("varlen_mixed", [1, 17, 128, 129, 5, 300], None, 64, 8, True, (-2, 2)),
+    ("mha_group1", [150, 33], None, 8, 8, True, (-2, 2)),
+    ("group2", [97], None, 16, 8, True, (-2, 2)),
+    ("group4", [211, 3], None, 16, 4, True, (-2, 2)),
+    ("group16", [77, 64], None, 64, 4, True, (-2, 2)),
+    ("group64", [40, 9], None, 64, 1, True, (-2, 2)),
+    ("noncausal", [90, 130], None, 64, 8, False, (-2, 2)),
+    ("append_lq_lt_lk", [37, 1, 64], [300, 20, 64], 64, 8, True, (-2, 2)),
+    ("lq_gt_lk", [80], [50], 64, 8, True, (-2, 2)),
+    ("empty_seq_in_batch", [0, 50, 0, 7], None, 64, 8, True, (-2, 2)),
+    ("strong_sinks", [160], None, 64, 8, True, (25, 30)),
+    ("weak_sinks", [160], None, 64, 8, True, (-30, -25)),
+    ("long_tiles", [1100], None, 64, 8, True, (-4, 4)),
+]
+
+
+@pytest.mark.parametrize("name,lq,lk,hq,hkv,causal,sr", PREFILL_SMALL, ids=[c[0] for c in PREFILL_SMALL])
+def test_prefill_bf16_small(name, lq, lk, hq, hkv, causal, sr):
+    sa = _sa()
+    case = workloads.make_prefill(lq, lk, num_q_heads=hq, num_kv_heads=hkv, sink_range=sr,
+                                  seed=_seed(name), causal=causal)
+    out = run_prefill(sa, case)
+    ref, _ = oracle_prefill(case)
+    check_bf16(out, ref, f"prefill {name}")
+    out32 = run_prefill(sa, case, out_dtype=torch.float32)
+    check_bf16(out32, ref, f"prefill {name} f32-out")
+
+
+def test_prefill_bf16_sink_neg_inf_is_plain_attention():
+    sa = _sa()
+    case = workloads.make_prefill([130, 64], num_q_heads=64, num_kv_heads=8, seed=7)
+    case.sinks[:] = float("-inf")
+    out = run_prefill(sa, case)
+    ref, _ = oracle_prefill(case)
+    check_bf16(out, ref, "prefill sink=-inf")
+
+
+def test_prefill_bf16_strided_views():
+    """q/k/v as views into one fused [T, Hq + 2 Hkv, D] buffer; out with padded head stride."""
+    sa = _sa()
+    case = workloads.make_prefill([150], num_q_heads=64, num_kv_heads=8, seed=11)
+    fused = torch.cat([case.q, case.k, case.v], dim=1).cuda()
+    q, k, v = fused[:, :64], fused[:, 64:72], fused[:, 72:80]
+    out_buf = torch.zeros(150, 64, 72, dtype=torch.bfloat16, device="cuda")
+    out = out_buf[:, :, :64]
+    sinks, cq, ck = _dev(case.sinks, case.cu_seqlens_q, case.cu_seqlens_k)
+    sa.prefill(q, k, v, sinks, cq, ck, case.scale, True, out=out)
+    torch.cuda.synchronize()
+    ref, _ = oracle_prefill(case)
+    check_bf16(out, ref, "prefill strided")
+    assert torch.all(out_buf[:, :, 64:] == 0), "padding between output rows was written"
+
+
+# ----------------------------------------------------------------------------- bf16 decode, small
+DECODE_SMALL = [
+    # (name, lens, cap, chunks, Hq, Hkv, sink_range, outlier_p)
+    ("uniform", [512, 512], 512, 4, 64, 8, (-2, 2), 0.0),
+    ("ragged_empty_chunks", [1, 0, 33, 700, 1023, 64], 1024, 8, 64, 8, (-2, 2), 0.0),
+    ("one_chunk", [300, 5], 320, 1, 64, 8, (-2, 2), 0.0),
+    ("many_chunks", [257, 100], 257, 40, 64, 8, (-2, 2), 0.0),
+    ("group1", [200, 31], 256, 4, 8, 8, (-2, 2), 0.0),
+    ("group2", [150], 160, 3, 16, 8, (-2, 2), 0.0),
+    ("group4", [99, 300], 300, 2, 16, 4, (-2, 2), 0.0),
+    ("group16", [333], 400, 5, 64, 4, (-2, 2), 0.0),
+    ("outliers", [2000, 1500], 2048, 2, 64, 8, (-4, 4), 0.02),
+    ("strong_sinks", [128, 64], 128, 2, 64, 8, (25, 30), 0.0),
+    ("weak_sinks", [128, 64], 128, 2, 64, 8, (-30, -25), 0.0),
+    ("kv_len_1", [1, 1, 1], 16, 4, 64, 8, (-2, 2), 0.0),
+]
+
+
+@pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,sr,op", DECODE_SMALL, ids=[c[0] for c in DECODE_SMALL])
+def test_decode_bf16_small(name, lens, cap, chunks, hq, hkv, sr, op):
+    sa = _sa()
+    # rows past each length are NaN: reading any of them would poison the output
+    case = workloads.make_decode(lens, cap, chunks, num_q_heads=hq, num_kv_heads=hkv, sink_range=sr,
+                                 outlier_p=op, seed=_seed(name), poison=True)
+    po, pm, pd, out, lse = run_decode(sa, case)
+    check_partials(po, pm, pd, case, check_bf16, f"decode {name}")
+    ref, rlse = oracle_decode(case)
+    check_bf16(out, ref, f"decode {name}")
+    np.testing.assert_allclose(_np(lse), rlse, rtol=0, atol=1e-3)
+
+
+def test_decode_bf16_sink_neg_inf_and_zero_length():
+    sa = _sa()
+    case = workloads.make_decode([0, 40, 0], 64, 4, seed=5, poison=True)
+    case.sinks[::2] = float("-inf")
+    po, pm, pd, out, lse = run_decode(sa, case)
+    check_partials(po, pm, pd, case, check_bf16, "decode -inf sinks")
+    ref, rlse = oracle_decode(case)
+    check_bf16(out, ref, "decode -inf sinks")
+    g = _np(lse)
+    assert np.array_equal(np.isneginf(g), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    np.testing.assert_allclose(g[fin], rlse[fin], atol=1e-3)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+
+
+def test_decode_equals_prefill_last_row_bf16():
+    """Decode of a sequence's last query row equals that row of causal prefill (on the GPU)."""
+    sa = _sa()
+    case = workloads.make_prefill([333], num_q_heads=64, num_kv_heads=8, seed=3)
+    pre = run_prefill(sa, case, out_dtype=torch.float32)
+    dec = workloads.DecodeCase(case.q[332:333].clone(), case.k.reshape(1, 333, 8, 64).clone(),
+                               case.v.reshape(1, 333, 8, 64).clone(), case.sinks.clone(),
+                               torch.tensor([333], dtype=torch.int32), 3)
+    _, _, _, out, _ = run_decode(sa, dec)
+    check_bf16(out[0], _np(pre)[332], "decode vs prefill last row")
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+def test_full_decode_workload_2():
+    sa = _sa()
+    case = workloads.make(2, poison=True).decode
+    po, pm, pd, out, lse = run_decode(sa, case)
+    ref, rlse = oracle_decode(case)
+    check_bf16(out, ref, "workload 2 decode")
+    np.testing.assert_allclose(_np(lse), rlse, atol=1e-3)
+
+
+def _decode_rows(case, pairs):
+    """Oracle decode for selected (b, kv-head) groups; returns {(b, g): out [G, D]}."""
+    group = case.q.shape[1] // case.k.shape[2]
+    res = {}
+    for b, g in pairs:
+        q = _np(case.q[b:b + 1, g * group:(g + 1) * group])
+        n = int(case.seqlens_k[b])
+        k = _np32(case.k[b:b + 1, :n, g:g + 1])
+        v = _np32(case.v[b:b + 1, :n, g:g + 1])
+        out, _ = oracle.decode(q, k, v, _np(case.sinks[g * group:(g + 1) * group]), [n], case.scale)
+        res[(b, g)] = out[0]
+    return res
+
+
+def test_full_long_decode_workload_4_sampled():
+    sa = _sa()
+    case = workloads.make(4, poison=True).decode
+    _, _, _, out, _ = run_decode(sa, case, return_lse=False)
+    rng = np.random.default_rng(4)
+    pairs = {(int(b), int(g)) for b, g in zip(rng.integers(0, 32, 24), rng.integers(0, 8, 24))}
+    pairs |= {(0, 0), (31, 7)}
+    ref = _decode_rows(case, sorted(pairs))
+    group = 8
+    g_out = np.stack([_np(out[b, g * group:(g + 1) * group]) for b, g in sorted(pairs)])
+    r_out = np.stack([ref[p] for p in sorted(pairs)])
+    check_bf16(torch.from_numpy(g_out), r_out, "workload 4 decode (sampled groups)")
+
+
+def _sampled_prefill(sa, case, n_samples, seed, label):
+    out = run_prefill(sa, case)
+    rng = np.random.default_rng(seed)
+    t_q = case.q.shape[0]
+    tokens = np.concatenate([rng.integers(0, t_q, n_samples), [0, t_q - 1]])
+    heads = np.concatenate([rng.integers(0, case.q.shape[1], n_samples), [0, case.q.shape[1] - 1]])
+    ref, _ = oracle.prefill_at(_np32(case.q), _np32(case.k), _np32(case.v), _np(case.sinks), case.cu_seqlens_q.numpy(),
+                               case.cu_seqlens_k.numpy(), case.scale, case.causal, tokens, heads)
+    g = out[torch.from_numpy(tokens).cuda(), torch.from_numpy(heads).cuda()]
+    check_bf16(g, ref, label)
+
+
+def test_full_prefill_workload_3_sampled():
+    sa = _sa()
+    case = workloads.make(3).prefill
+    _sampled_prefill(sa, case, 400, 3, "workload 3 prefill (sampled rows)")
+
+
+def test_full_mixed_workload_5():
+    sa = _sa()
+    w = workloads.make(5, poison=True)
+    po, pm, pd, out, lse = run_decode(sa, w.decode)
+    ref, rlse = oracle_decode(w.decode)
+    check_bf16(out, ref, "workload 5 decode")
+    _sampled_prefill(sa, w.prefill, 400, 5, "workload 5 prefill (sampled rows)")

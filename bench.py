@@ -59,17 +59,37 @@ def _traffic_from_profile(kernel_hash):
     return float(t.group(1))
 
 
-def _time_loop(fn, iters, torch):
-    """Average ms per call of ``fn(i)`` over ``iters`` back-to-back calls on the current stream."""
+def _capture(fn, calls, torch):
+    """A HIP graph holding ``calls`` back-to-back calls ``fn(0) .. fn(calls - 1)``.
+
+    Replaying it issues the kernels without Python or ctypes in between, so event timings see
+    GPU time (plus the small inter-kernel dispatch gap) rather than host launch overhead.
+    """
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(calls):
+            fn(i)
+    return graph
+
+
+def _time_graph(graph, calls, torch, replays=3):
+    """Average ms per captured call over ``replays`` replays, events on the replay stream."""
+    graph.replay()
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
-    for i in range(iters):
-        fn(i)
+    for _ in range(replays):
+        graph.replay()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / iters
+    return start.elapsed_time(end) / (replays * calls)
 
 
 def cpu_baseline(case, kv_bytes):
@@ -166,15 +186,35 @@ def main():
     _log(f"decode: {n_sets} rotating K/V sets of {set_bytes / 2**20:.0f} MiB; warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
+    steps_graph = _capture(step, args.steps, torch)
+    steps_graph.replay()  # untimed: first replay uploads the graph
     torch.cuda.synchronize()
-    # Timed region: exactly `steps` steps, synchronised on both sides.
+    # Timed region: exactly `steps` steps (one replay of the captured steps), synchronised and
+    # event-bracketed on both sides.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ms_step = _time_loop(step, args.steps, torch)
+    start.record()
+    steps_graph.replay()
+    end.record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    _log(f"decode step {ms_step * 1e3:.2f} us ({wall:.3f} s wall for {args.steps} steps)")
-    ms_split = _time_loop(split, max(args.steps, 50), torch)
-    ms_merge = _time_loop(merge, max(args.steps, 50), torch)
-    ms_hot = _time_loop(step_hot, max(args.steps, 50), torch)
+    ms_step = start.elapsed_time(end) / args.steps
+    _log(f"decode step {ms_step * 1e3:.2f} us ({wall * 1e3:.2f} ms wall for {args.steps} steps)")
+    n_rep = max(args.steps, 50)
+    ms_split = _time_graph(_capture(split, n_rep, torch), n_rep, torch)
+    ms_merge = _time_graph(_capture(merge, n_rep, torch), n_rep, torch)
+    ms_hot = _time_graph(_capture(step_hot, n_rep, torch), n_rep, torch)
+    ms_eager = None
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_rep):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / n_rep
     value = step_bytes / (ms_step * 1e-3) / 1e9
     split_gbs = split_bytes / (ms_split * 1e-3) / 1e9
     _log(f"split {ms_split * 1e3:.2f} us ({split_gbs:.0f} GB/s), merge {ms_merge * 1e3:.2f} us, "
@@ -214,6 +254,8 @@ def main():
         "decode_detail": {
             "split_us": round(ms_split * 1e3, 3), "merge_us": round(ms_merge * 1e3, 3),
             "step_us_rotated": round(ms_step * 1e3, 3), "step_us_hot": round(ms_hot * 1e3, 3),
+            "step_us_eager_python_launch": round(ms_eager * 1e3, 3),
+            "timing": "HIP graph replay of back-to-back calls, events on the replay stream",
             "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         },
     }
@@ -234,7 +276,8 @@ def main():
 
         for i in range(max(2, args.warmup // 2)):
             prefill(i)
-        ms_pre = _time_loop(prefill, max(5, args.steps // 2), torch)
+        n_pre = max(5, args.steps // 2)
+        ms_pre = _time_graph(_capture(prefill, n_pre, torch), n_pre, torch, replays=2)
         tflops = flops / (ms_pre * 1e-3) / 1e12
         _log(f"prefill {ms_pre * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
         result["prefill"] = {

@@ -338,6 +338,10 @@ sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_t
                     (long long)group);
     if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    // Cache rows of one (sequence, KV head) slice are addressed with 32-bit byte offsets.
+    if (cap * k->stride[1] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
+        cap * v->stride[1] * elem_size(v->dtype) >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "KV cache slice of one sequence exceeds 2 GiB");
 
     SA_TRY(check_data(q, "q"));
     SA_TRY(check_data(k, "k"));

@@ -11,13 +11,14 @@
 // work-group, four waves take interleaved 32-key blocks of the chunk and keep their own softmax
 // state; the states are merged through LDS at the end and written as the chunk's (m, d, o).
 //
-// Per 32-key block, per wave:
-//   S^T (32 keys x 16 heads) = K (32 x 64) . Q^T (64 x 16): 4 MFMA 16x16x32, K straight from HBM
-//     (128-bit loads, 16 lanes x 16 bytes cover a key row segment), Q^T resident in registers.
+// Per 64-key block, per wave (the next block's loads are in flight meanwhile):
+//   S^T (64 keys x 16 heads) = K (64 x 64) . Q^T (64 x 16): 8 MFMA 16x16x32, K straight from HBM
+//     into operand registers (128-bit loads), Q^T resident in registers.
 //   Online softmax on S^T columns in the log2 domain (scale and sink pre-multiplied by log2 e).
-//   O^T (64 d x 16 heads) += V^T (64 x 32) . P^T (32 x 16): 4 MFMA 16x16x32. P^T comes straight
-//     from the S^T accumulator registers (same lanes, same columns); V^T is staged through a
-//     wave-private LDS tile, written transposed.
+//   O^T (64 d x 16 heads) += V^T (64 x 64) . P^T (64 x 16): 8 MFMA 16x16x32. P^T comes straight
+//     from the S^T accumulator registers (same lanes, same columns); V goes row-major into a
+//     wave-private LDS tile (128-bit writes) and comes back transposed through the gfx950
+//     transpose read, so no element-wise transposition is needed.
 
 #include "device_common.h"
 #include "launch.h"
@@ -27,28 +28,133 @@ namespace {
 
 constexpr int kSplitWaves = 4;
 constexpr int kSplitThreads = kSplitWaves * 64;
-constexpr int kKeysPerBlock = 32;
-// V^T tile row pitch in bf16 elements: 32 keys + 8 pad (80 bytes = 20 dwords). Rows stay 8-byte
-// aligned for the 64-bit operand reads, which then hit 64 distinct banks per 32 lanes; the
-// transposed 2-byte writes see at most 2-way bank conflicts.
-constexpr int kVtPitch = 40;
+constexpr int kBlockKeys = 64;  // keys per wave iteration
+// V tile row pitch in bf16 elements: 64 + 16 pad = 160 bytes = 40 dwords. The transpose reads of
+// 8 consecutive rows then start on 8 disjoint 8-bank groups (conflict-free per half-wave).
+constexpr int kVPitch = 80;
 
-__global__ __launch_bounds__(kSplitThreads) void decode_split_bf16_kernel(DecodeSplitParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 vt_tile[kSplitWaves][kHeadDim][kVtPitch];
+// One wave's share of a 64-key block: lane (col, grp) holds key rows base + 16t + col (t = 0..3),
+// 16-byte segments grp and grp + 4 of each row, for K and for V.
+struct KvBlock {
+    bf16x8 k[4][2];
+    bf16x8 v[4][2];
+};
+
+// Keys at or past the chunk end fall outside the buffer ranges and load as zeros.
+__device__ __forceinline__ void load_block(KvBlock& r, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                           uint32_t k_row_bytes, uint32_t v_row_bytes, uint32_t base,
+                                           int col, int grp) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t key = base + 16 * t + col;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t off = 16 * (grp + 4 * h);
+            r.k[t][h] = buffer_load_x8(krs, key * k_row_bytes + off);
+            r.v[t][h] = buffer_load_x8(vrs, key * v_row_bytes + off);
+        }
+    }
+}
+
+struct SplitState {
+    f32x4 acc[4];  // O^T block n: rows d = 16n + 4grp + i, column = head col
+    float m;       // running max, log2 units (uniform over the column's four lanes)
+    float dsum;    // this lane's share of the running scale d
+};
+
+// Folds one 64-key block into the wave's state.
+//   S^T (64 x 16) = K . Q^T with K straight from registers;
+//   P^T k-slots for key group u (32 keys): slots 0..3 = keys 32u + 4grp + e (S^T block 2u),
+//   slots 4..7 = keys 32u + 16 + 4grp + e (S^T block 2u + 1), which is where this lane's S^T
+//   values already sit; V^T operands come from the wave's row-major V tile via transpose reads.
+__device__ __forceinline__ void fold_block(SplitState& st, const KvBlock& r, const bf16x8 (&q_op)[2],
+                                           __bf16 (*vl)[kVPitch], int base, int hi,
+                                           float c2, int col, int grp) {
+    lds_order();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<bf16x8*>(&vl[16 * t + col][8 * (grp + 4 * h)]) = r.v[t][h];
+
+    f32x4 s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        s[t] = mfma16x16x32(r.k[t][0], q_op[0], zero_f32x4());
+        s[t] = mfma16x16x32(r.k[t][1], q_op[1], s[t]);
+    }
+    const bool tail = base + kBlockKeys > hi;
+    float x[16];
+    float bmax = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = s[t][i] * c2;
+            if (tail && base + 16 * t + 4 * grp + i >= hi) v = kNegInf;
+            x[4 * t + i] = v;
+            bmax = fmaxf(bmax, v);
+        }
+    bmax = max_over_groups(bmax);
+    const float m_new = fmaxf(st.m, bmax);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = exp2_fast(st.m - m_use);
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        x[e] = exp2_fast(x[e] - m_use);
+        psum += x[e];
+    }
+    st.dsum = st.dsum * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) st.acc[n] *= alpha;
+
+    bf16x8 p_op[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p_op[u][e] = (__bf16)x[4 * (2 * u) + e];
+            p_op[u][4 + e] = (__bf16)x[4 * (2 * u + 1) + e];
+        }
+
+    lds_order();
+    // Transpose-read addressing: lane (grp, col) points at row 4grp + col/4 (+16 for slots 4..7)
+    // and columns 16n + 4(col%4); it receives column 16n + col of rows 4grp + 0..3.
+    const int tr_row = 4 * grp + (col >> 2);
+    const int tr_col = 4 * (col & 3);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const bf16x4 lo4 = lds_read_tr4(&vl[32 * u + tr_row][16 * n + tr_col]);
+            const bf16x4 hi4 = lds_read_tr4(&vl[32 * u + 16 + tr_row][16 * n + tr_col]);
+            const bf16x8 v_op = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.acc[n] = mfma16x16x32(v_op, p_op[u], st.acc[n]);
+        }
+    lds_order();
+}
+
+__global__ __launch_bounds__(kSplitThreads, 2) void decode_split_bf16_kernel(DecodeSplitParams p) {
+    __shared__ __attribute__((aligned(16))) __bf16 v_tile[kSplitWaves][kBlockKeys][kVPitch];
     __shared__ __attribute__((aligned(16))) float red_m[kSplitWaves][16];
     __shared__ __attribute__((aligned(16))) float red_d[kSplitWaves][16];
     __shared__ __attribute__((aligned(16))) float red_o[kSplitWaves][16][kHeadDim + 4];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // Wave index in an SGPR: the block loop below is then wave-uniform control flow.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;  // MFMA column: query head within the group
     const int grp = lane >> 4;  // k-slot group / row quad
 
+    // KV head fastest: the work-groups that read the Hkv interleaved 128-byte slices of the same
+    // cache rows are dispatched together.
     int bid = blockIdx.x;
-    const int chunk = bid % p.num_chunks;
-    bid /= p.num_chunks;
     const int g = bid % p.num_kv_heads;
-    const int b = bid / p.num_kv_heads;
+    bid /= p.num_kv_heads;
+    const int chunk = bid % p.num_chunks;
+    const int b = bid / p.num_chunks;
     const int group = p.num_q_heads / p.num_kv_heads;
     const bool col_valid = col < group;
     const int head = g * group + (col_valid ? col : 0);
@@ -65,106 +171,58 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_bf16_kernel(Decode
         q_op[h] = col_valid ? *reinterpret_cast<const bf16x8*>(qbase + 32 * h + 8 * grp) : zero_bf16x8();
 
     const float c2 = p.scale * kLog2e;
-    float m = kNegInf;
-    float dsum = 0.0f;
+    SplitState st;
+    st.m = kNegInf;
+    st.dsum = 0.0f;
     if (chunk == 0 && wave == 0) {
         // The first chunk starts from the sink: m = sink (log2 units), d = 1 = e^(sink - sink).
-        m = p.sinks[head] * kLog2e;
-        dsum = (grp == 0 && m != kNegInf) ? 1.0f : 0.0f;
+        st.m = p.sinks[head] * kLog2e;
+        st.dsum = (grp == 0 && st.m != kNegInf) ? 1.0f : 0.0f;
     }
-    f32x4 acc[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[n] = zero_f32x4();
+    for (int n = 0; n < 4; ++n) st.acc[n] = zero_f32x4();
 
+    // Buffer ranges end at the chunk end: rows [0, hi) of this (sequence, KV head) slice.
     const __bf16* kbase = static_cast<const __bf16*>(p.k) + b * p.k_stride_b + g * p.k_stride_head;
     const __bf16* vbase = static_cast<const __bf16*>(p.v) + b * p.v_stride_b + g * p.v_stride_head;
-    __bf16(*vt)[kVtPitch] = vt_tile[wave];
+    const uint32_t k_row_bytes = static_cast<uint32_t>(p.k_stride_tok * 2);
+    const uint32_t v_row_bytes = static_cast<uint32_t>(p.v_stride_tok * 2);
+    const __amdgpu_buffer_rsrc_t krs = make_buffer(kbase, static_cast<uint32_t>(hi) * k_row_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_buffer(vbase, static_cast<uint32_t>(hi) * v_row_bytes);
+    __bf16(*vl)[kVPitch] = v_tile[wave];
 
-    for (int64_t base = lo + wave * kKeysPerBlock; base < hi; base += kSplitWaves * kKeysPerBlock) {
-        // Lane (col, grp) owns key rows base + 16t + col (t = 0, 1) and the 16-byte segments
-        // grp and grp + 4 of each row.
-        bf16x8 kreg[2][2], vreg[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int64_t key = base + 16 * t + col;
-            const bool ok = key < hi;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int off = 8 * (grp + 4 * h);
-                kreg[t][h] = ok ? *reinterpret_cast<const bf16x8*>(kbase + key * p.k_stride_tok + off)
-                                : zero_bf16x8();
-                vreg[t][h] = ok ? *reinterpret_cast<const bf16x8*>(vbase + key * p.v_stride_tok + off)
-                                : zero_bf16x8();
-            }
-        }
-        // V^T into the wave's LDS tile: element (key 16t + col, d = 8*(grp + 4h) + e).
-        lds_order();
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vt[8 * (grp + 4 * h) + e][16 * t + col] = vreg[t][h][e];
-
-        // S^T blocks: rows = keys base + 16t + 4grp + i, column = head col.
-        f32x4 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = mfma16x16x32(kreg[t][0], q_op[0], zero_f32x4());
-            s[t] = mfma16x16x32(kreg[t][1], q_op[1], s[t]);
-        }
-        float x[8];
-        float bmax = kNegInf;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t key = base + 16 * t + 4 * grp + i;
-                const float v = key < hi ? s[t][i] * c2 : kNegInf;
-                x[4 * t + i] = v;
-                bmax = fmaxf(bmax, v);
-            }
-        bmax = max_over_groups(bmax);
-        const float m_new = fmaxf(m, bmax);
-        const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = exp2_fast(m - m_use);
-        float psum = 0.0f;
-        bf16x8 p_op;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = exp2_fast(x[e] - m_use);
-            psum += pe;
-            p_op[e] = (__bf16)pe;
-        }
-        dsum = dsum * alpha + psum;
-        m = m_new;
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[n] *= alpha;
-
-        lds_order();
-        // O^T block n: rows d = 16n + col; k-slots e < 4 are keys 4grp + e, e >= 4 are keys
-        // 16 + 4grp + (e - 4): exactly the keys whose P values this lane holds.
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const __bf16* row = vt[16 * n + col];
-            bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(row + 4 * grp);
-            bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(row + 16 + 4 * grp);
-            bf16x8 v_op = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[n] = mfma16x16x32(v_op, p_op, acc[n]);
-        }
-        lds_order();
+    // Blocks of this wave: base = lo + 64 * (wave + 4 i). Two register sets alternate so the next
+    // block's 16 loads per lane are in flight while the current block is folded. The prefetch is
+    // unconditional: past the chunk end it returns zeros without touching memory.
+    constexpr uint32_t kStride = kSplitWaves * kBlockKeys;
+    uint32_t base = static_cast<uint32_t>(lo) + wave * kBlockKeys;
+    const uint32_t end = static_cast<uint32_t>(hi);
+    // The scheduling barriers keep each prefetch ahead of the math that waits on the previous
+    // block, so two blocks' loads are in flight at every wait.
+    KvBlock ra, rb;
+    load_block(ra, krs, vrs, k_row_bytes, v_row_bytes, base, col, grp);
+    while (base < end) {
+        load_block(rb, krs, vrs, k_row_bytes, v_row_bytes, base + kStride, col, grp);
+        __builtin_amdgcn_sched_barrier(0);
+        fold_block(st, ra, q_op, vl, static_cast<int>(base), static_cast<int>(hi), c2, col, grp);
+        base += kStride;
+        if (base >= end) break;
+        load_block(ra, krs, vrs, k_row_bytes, v_row_bytes, base + kStride, col, grp);
+        __builtin_amdgcn_sched_barrier(0);
+        fold_block(st, rb, q_op, vl, static_cast<int>(base), static_cast<int>(hi), c2, col, grp);
+        base += kStride;
     }
 
     // Merge the four waves' states (log2 domain) and write the chunk's (m, d, o).
-    const float d_wave = sum_over_groups(dsum);
+    const float d_wave = sum_over_groups(st.dsum);
     if (grp == 0) {
-        red_m[wave][col] = m;
+        red_m[wave][col] = st.m;
         red_d[wave][col] = d_wave;
     }
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red_o[wave][col][16 * n + 4 * grp + i] = acc[n][i];
+        for (int i = 0; i < 4; ++i) red_o[wave][col][16 * n + 4 * grp + i] = st.acc[n][i];
     __syncthreads();
 
     for (int idx = threadIdx.x; idx < group * kHeadDim; idx += kSplitThreads) {

@@ -9,6 +9,7 @@ namespace sinkattn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -24,6 +25,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes, result lane i,
+// element e is element (i % 4) of the 8-byte row addressed by lane 4 * e + i / 4 of the same
+// group. So if lane 4e + j of a group points at row r_e, columns c0 + 4j .. c0 + 4j + 3 of a
+// row-major bf16 tile, lane i receives column c0 + i of rows r_0 .. r_3: a 4 x 16 block comes
+// back transposed, ready as 4 k-slots of an MFMA operand.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(const_cast<__bf16*>(p)));
+}
 
 // Lane-crossing max/sum over the lanes l, l^16, l^32, l^48 (the four k-slot groups of one MFMA
 // column).
@@ -47,6 +58,20 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 }
 
 __device__ __forceinline__ f32x4 zero_f32x4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// Raw buffer resource over [base, base + num_bytes). A buffer load whose offset lies past
+// num_bytes returns zeros and makes no memory access, so tails and prefetches past the end need
+// neither a branch nor an exec-mask change (branch-free loads also let the compiler keep exact
+// s_waitcnt vmcnt counts across a software-pipelined loop). Dword 3 = 0x00020000 selects the
+// 32-bit data format that gfx9-family raw buffer accesses require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(num_bytes), 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buffer_load_x8(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_offset, 0, 0));
+}
 
 // Compiler-level ordering of LDS accesses made by one wave. The hardware executes one wave's LDS
 // instructions in order, so a wave-private LDS region needs no s_barrier.

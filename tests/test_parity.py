@@ -312,3 +312,45 @@ def test_full_mixed_workload_5():
     ref, rlse = oracle_decode(w.decode)
     check_bf16(out, ref, "workload 5 decode")
     _sampled_prefill(sa, w.prefill, 400, 5, "workload 5 prefill (sampled rows)")
+
+
+def test_graph_replays_match_eager():
+    """The kernels captured in a HIP graph give the eager result on every replay."""
+    sa = _sa()
+    dec = workloads.make_decode([700, 33, 1024, 0], 1024, 8, seed=21)
+    pre = workloads.make_prefill([300, 77], seed=22)
+    q, k, v, s, sl = _dev(dec.q, dec.k, dec.v, dec.sinks, dec.seqlens_k)
+    pq, pk, pv, ps, cq, ck = _dev(pre.q, pre.k, pre.v, pre.sinks, pre.cu_seqlens_q, pre.cu_seqlens_k)
+    po = torch.empty((4, 64, 8, 64), dtype=torch.float32, device="cuda")
+    pm = torch.empty((4, 64, 8), dtype=torch.float32, device="cuda")
+    pd = torch.empty((4, 64, 8), dtype=torch.float32, device="cuda")
+    out = torch.empty((4, 64, 64), dtype=torch.bfloat16, device="cuda")
+    pout = torch.empty_like(pq)
+
+    def work():
+        sa.decode_split(q, k, v, s, sl, 8, dec.scale, po, pm, pd)
+        sa.decode_merge(po, pm, pd, out=out)
+        sa.prefill(pq, pk, pv, ps, cq, ck, pre.scale, True, out=pout)
+
+    work()
+    torch.cuda.synchronize()
+    eager_dec, eager_pre = out.clone(), pout.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(4):
+        out.zero_()
+        pout.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_dec), f"decode differs on replay {rep}"
+        assert torch.equal(pout, eager_pre), f"prefill differs on replay {rep}"
+        work()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_dec)

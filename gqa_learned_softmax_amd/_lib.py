@@ -68,7 +68,7 @@ EXPORTS = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m gqa_learned_softmax_amd.build` "
+            f"{LIB_PATH} is not built; run `python gqa_learned_softmax_amd/build.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (argtypes, restype) in EXPORTS.items():

@@ -1,6 +1,6 @@
 """Builds libsinkattn.so (the C-ABI HIP library) in-tree with hipcc for gfx950.
 
-Usage: ``python -m gqa_learned_softmax_amd.build`` (or ``build()`` from Python). Sources are
+Usage: ``python gqa_learned_softmax_amd/build.py`` (or ``__graft_entry__.build()``). Sources are
 compiled to objects in parallel, then linked into ``gqa_learned_softmax_amd/libsinkattn.so``.
 Every call recompiles.
 """

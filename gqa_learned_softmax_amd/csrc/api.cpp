@@ -239,6 +239,11 @@ sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor
                     (long long)group);
     if (tq >= (int64_t(1) << 31) || tk >= (int64_t(1) << 31) || num_seqs >= (int64_t(1) << 24))
         return fail(SINKATTN_ERR_UNSUPPORTED, "token or sequence count too large");
+    // Key rows are addressed with 32-bit byte offsets, including prefetches up to 128 rows past
+    // a sequence's end.
+    if ((tk + 128) * k->stride[0] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
+        (tk + 128) * v->stride[0] * elem_size(v->dtype) >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "K/V exceed 2 GiB of addressable rows");
 
     SA_TRY(check_data(q, "q"));
     SA_TRY(check_data(k, "k"));
@@ -338,9 +343,10 @@ sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_t
                     (long long)group);
     if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
-    // Cache rows of one (sequence, KV head) slice are addressed with 32-bit byte offsets.
-    if (cap * k->stride[1] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
-        cap * v->stride[1] * elem_size(v->dtype) >= (int64_t(1) << 31))
+    // Cache rows of one (sequence, KV head) slice are addressed with 32-bit byte offsets,
+    // including prefetches up to 512 rows past a chunk end.
+    if ((cap + 512) * k->stride[1] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
+        (cap + 512) * v->stride[1] * elem_size(v->dtype) >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "KV cache slice of one sequence exceeds 2 GiB");
 
     SA_TRY(check_data(q, "q"));

@@ -8,6 +8,7 @@ namespace sinkattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -24,6 +25,23 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A (32x16) times B (16x32), bf16 inputs, fp32 32x32 accumulator: v_mfma_f32_32x32x16_bf16.
+// Lane l: A holds row (l % 32) and 8 k-slots of group (l / 32); B holds column (l % 32) and the
+// same k-slots; result register r holds row 8 * (r / 4) + 4 * (l / 32) + (r % 4) of column
+// (l % 32). On gfx950 this shape sustains close to twice the throughput of the 16x16x32 one.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // gfx950 LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes, result lane i,
@@ -36,19 +54,33 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
         (__attribute__((address_space(3))) bf16x4*)(const_cast<__bf16*>(p)));
 }
 
-// Lane-crossing max/sum over the lanes l, l^16, l^32, l^48 (the four k-slot groups of one MFMA
-// column).
-__device__ __forceinline__ float max_over_groups(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+// Values of lanes l ^ 32 and l ^ 16 through the gfx950 lane-swap instructions (VALU only, no LDS
+// round trip). With both operands equal, v_permlane32_swap returns the low half duplicated and the
+// high half duplicated, so every lane sees its own value and its partner's.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float sum_over_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max/sum over the lanes l, l^16, l^32, l^48 (the four k-slot groups of one 16x16 MFMA column).
+__device__ __forceinline__ float max_over_groups(float x) { return max_xor32(max_xor16(x)); }
+
+__device__ __forceinline__ float sum_over_groups(float x) { return sum_xor32(sum_xor16(x)); }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
     bf16x8 z;
@@ -71,6 +103,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, 
 
 __device__ __forceinline__ bf16x8 buffer_load_x8(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_offset, 0, 0));
+}
+
+// acc + p[0] + p[1] in fp32 with one v_dot2c_f32_bf16 against (1, 1).
+__device__ __forceinline__ float sum_bf16x2(bf16x2 p, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+}
+
+// Scheduling hint for the current scheduling region: alternate one MFMA with kValu VALU
+// instructions, kMfma times, so the matrix core and the vector ALU of one wave stay busy together.
+template <int kMfma, int kValu>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+    }
 }
 
 // Compiler-level ordering of LDS accesses made by one wave. The hardware executes one wave's LDS

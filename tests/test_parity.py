@@ -151,6 +151,10 @@ PREFILL_SMALL = [
     ("strong_sinks", [160], None, 64, 8, True, (25, 30)),
     ("weak_sinks", [160], None, 64, 8, True, (-30, -25)),
     ("long_tiles", [1100], None, 64, 8, True, (-4, 4)),
+    ("tile_edges", [31, 32, 33, 63, 64, 65, 255, 256, 257], None, 64, 8, True, (-2, 2)),
+    ("mha_long", [700], None, 4, 4, True, (-2, 2)),
+    ("group128", [20, 3], None, 128, 1, True, (-2, 2)),
+    ("append_long", [100], [2000], 64, 8, True, (-2, 2)),
 ]
 
 

@@ -34,17 +34,23 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of bf16 MFMA peak)"
 ROTATE_BYTES = 512 * 2**20
+CALIB_BYTES = 256 * 2**20
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_b8_len8192_pmc.txt")
-SPLIT_SOURCE = os.path.join(ROOT, "gqa_learned_softmax_amd", "csrc", "decode_split.hip")
+# The split kernel's complete source: its traffic figure is only reused while these are unchanged.
+SPLIT_SOURCES = [os.path.join(ROOT, "gqa_learned_softmax_amd", "csrc", f)
+                 for f in ("decode_split.hip", "device_common.h", "launch.h")]
 
 
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def _source_hash(path):
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def _source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic_from_profile(kernel_hash):
@@ -131,6 +137,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--hot", action="store_true",
+                    help="also time steps that reuse one K/V set (cache-resident; not the headline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the hot path here is a "
@@ -144,6 +152,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- counter calibration
+    # One plain device-to-device copy of known size (256 MiB read + 256 MiB written). Under
+    # rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the scale from counter units to bytes.
+    calib_src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     # ---------------------------------------------------------------- decode workload (value)
     _log("generating decode workload (8 x 8192, 64/8 heads, bf16)")
@@ -204,7 +221,7 @@ def main():
     n_rep = max(args.steps, 50)
     ms_split = _time_graph(_capture(split, n_rep, torch), n_rep, torch)
     ms_merge = _time_graph(_capture(merge, n_rep, torch), n_rep, torch)
-    ms_hot = _time_graph(_capture(step_hot, n_rep, torch), n_rep, torch)
+    ms_hot = _time_graph(_capture(step_hot, n_rep, torch), n_rep, torch) if args.hot else None
     ms_eager = None
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -217,10 +234,10 @@ def main():
     ms_eager = e0.elapsed_time(e1) / n_rep
     value = step_bytes / (ms_step * 1e-3) / 1e9
     split_gbs = split_bytes / (ms_split * 1e-3) / 1e9
-    _log(f"split {ms_split * 1e3:.2f} us ({split_gbs:.0f} GB/s), merge {ms_merge * 1e3:.2f} us, "
-         f"hot step {ms_hot * 1e3:.2f} us")
+    _log(f"split {ms_split * 1e3:.2f} us ({split_gbs:.0f} GB/s), merge {ms_merge * 1e3:.2f} us"
+         + (f", hot step {ms_hot * 1e3:.2f} us" if ms_hot else ""))
 
-    traffic = _traffic_from_profile(_source_hash(SPLIT_SOURCE))
+    traffic = _traffic_from_profile(_source_hash(SPLIT_SOURCES))
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -253,7 +270,8 @@ def main():
         },
         "decode_detail": {
             "split_us": round(ms_split * 1e3, 3), "merge_us": round(ms_merge * 1e3, 3),
-            "step_us_rotated": round(ms_step * 1e3, 3), "step_us_hot": round(ms_hot * 1e3, 3),
+            "step_us_rotated": round(ms_step * 1e3, 3),
+            "step_us_hot": round(ms_hot * 1e3, 3) if ms_hot else None,
             "step_us_eager_python_launch": round(ms_eager * 1e3, 3),
             "timing": "HIP graph replay of back-to-back calls, events on the replay stream",
             "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

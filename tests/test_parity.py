@@ -210,6 +210,10 @@ DECODE_SMALL = [
     ("strong_sinks", [128, 64], 128, 2, 64, 8, (25, 30), 0.0),
     ("weak_sinks", [128, 64], 128, 2, 64, 8, (-30, -25), 0.0),
     ("kv_len_1", [1, 1, 1], 16, 4, 64, 8, (-2, 2), 0.0),
+    ("odd_kv_heads", [300, 77], 320, 4, 12, 3, (-2, 2), 0.0),
+    # B * Hkv/2 * C = 256 with a token-major cache: the two-KV-heads-per-work-group kernel
+    ("paired_heads", [250, 3, 0, 129], 256, 16, 64, 8, (-2, 2), 0.0),
+    ("single_kv_head", [500, 64], 512, 3, 16, 1, (-2, 2), 0.0),
 ]
 
 

@@ -14,7 +14,8 @@ import torch
 from . import _lib
 from ._lib import SinkAttnError  # noqa: F401
 
-__all__ = ["prefill", "decode_split", "decode_merge", "decode", "SinkAttnError", "version"]
+__all__ = ["prefill", "decode_split", "decode_merge", "decode", "decode_fused", "decode_workspace",
+           "SinkAttnError", "version"]
 
 
 def version() -> int:
@@ -73,3 +74,26 @@ def decode(q, k, v, sinks, seqlens_k, num_chunks, scale, out=None, return_lse=Fa
     """Split then merge on the current stream (partials allocated with torch)."""
     po, pm, pd = decode_split(q, k, v, sinks, seqlens_k, num_chunks, scale)
     return decode_merge(po, pm, pd, out=out, out_dtype=q.dtype, return_lse=return_lse)
+
+
+def decode_workspace(batch, num_q_heads, num_kv_heads, num_chunks, device):
+    """A zeroed workspace for ``decode_fused`` (reusable across calls on one stream)."""
+    size = _lib.lib.sinkattn_decode_workspace_size(batch, num_q_heads, num_kv_heads, num_chunks)
+    return torch.zeros(max(int(size), 1), dtype=torch.uint8, device=device)
+
+
+def decode_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, out=None, lse=None,
+                 return_lse=False):
+    """``sinkattn_decode``: split-KV decode and merge in one launch; out [B, Hq, D]."""
+    batch, hq, dim = q.shape
+    if out is None:
+        out = torch.empty((batch, hq, dim), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, seqlens_k, workspace, out, lse)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k, out, lse)]
+    _lib.check(_lib.lib.sinkattn_decode(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        int(num_chunks), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out

@@ -187,6 +187,95 @@ sinkattn_status launched(hipError_t err) {
     return SINKATTN_OK;
 }
 
+// Validation shared by sinkattn_decode_split and sinkattn_decode: the inputs, chunking and scale.
+// Fills the input half of `p`.
+sinkattn_status check_decode_inputs(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                    const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                    const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                    sinkattn::DecodeSplitParams& p) {
+    SA_TRY(check_desc(q, "q", 3));
+    SA_TRY(check_desc(k, "k", 4));
+    SA_TRY(check_desc(v, "v", 4));
+    if (q->dtype != SINKATTN_BF16 && q->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "q: dtype must be bf16 or f32");
+    SA_TRY(check_dtype(k, "k", q->dtype));
+    SA_TRY(check_dtype(v, "v", q->dtype));
+
+    const int64_t batch = q->shape[0], hq = q->shape[1], dim = q->shape[2];
+    const int64_t cap = k->shape[1], hkv = k->shape[2];
+    for (int i = 0; i < 4; ++i)
+        if (v->shape[i] != k->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, "v: shape differs from k");
+    if (k->shape[0] != batch) return fail(SINKATTN_ERR_SHAPE, "k: batch differs from q");
+    if (k->shape[3] != dim) return fail(SINKATTN_ERR_SHAPE, "k: head_dim differs from q");
+    if (hkv <= 0 || hq <= 0 || hq % hkv != 0)
+        return fail(SINKATTN_ERR_SHAPE, "query heads (%lld) must be a positive multiple of KV heads (%lld)",
+                    (long long)hq, (long long)hkv);
+    if (num_chunks < 1) return fail(SINKATTN_ERR_SHAPE, "num_chunks must be >= 1 (got %d)", num_chunks);
+    SA_TRY(check_vec(seqlens_k, "seqlens_k", SINKATTN_I32, batch));
+    SA_TRY(check_vec(sinks, "sinks", SINKATTN_F32, hq));
+    SA_TRY(check_scale(scale));
+    if (dim != sinkattn::kHeadDim)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (only 64)", (long long)dim);
+    const int64_t group = hq / hkv;
+    if (!is_pow2(group) || group > 16)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "group size %lld not supported (1, 2, 4, 8 or 16)",
+                    (long long)group);
+    if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    // Cache rows of one (sequence, KV head) slice are addressed with 32-bit byte offsets,
+    // including prefetches up to 512 rows past a chunk end.
+    if ((cap + 512) * k->stride[1] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
+        (cap + 512) * v->stride[1] * elem_size(v->dtype) >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "KV cache slice of one sequence exceeds 2 GiB");
+    SA_TRY(check_data(q, "q"));
+    SA_TRY(check_data(k, "k"));
+    SA_TRY(check_data(v, "v"));
+    SA_TRY(check_rows(q, "q"));
+    SA_TRY(check_rows(k, "k"));
+    SA_TRY(check_rows(v, "v"));
+
+    p.q = q->data;
+    p.k = k->data;
+    p.v = v->data;
+    p.sinks = static_cast<const float*>(sinks->data);
+    p.seqlens_k = static_cast<const int32_t*>(seqlens_k->data);
+    p.q_stride_b = q->stride[0];
+    p.q_stride_head = q->stride[1];
+    p.k_stride_b = k->stride[0];
+    p.k_stride_tok = k->stride[1];
+    p.k_stride_head = k->stride[2];
+    p.v_stride_b = v->stride[0];
+    p.v_stride_tok = v->stride[1];
+    p.v_stride_head = v->stride[2];
+    p.capacity = cap;
+    p.chunk_size = (cap + num_chunks - 1) / num_chunks;
+    p.batch = static_cast<int32_t>(batch);
+    p.num_q_heads = static_cast<int32_t>(hq);
+    p.num_kv_heads = static_cast<int32_t>(hkv);
+    p.num_chunks = num_chunks;
+    p.scale = scale;
+    return SINKATTN_OK;
+}
+
+// Byte offsets of the fused-decode workspace regions (each 256-byte aligned).
+struct WorkspaceLayout {
+    size_t counters = 0, partial_o = 0, partial_m = 0, partial_d = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+WorkspaceLayout workspace_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t chunks) {
+    WorkspaceLayout w;
+    const size_t rows = static_cast<size_t>(batch) * hq * chunks;
+    w.counters = 0;
+    w.partial_o = align256(static_cast<size_t>(batch) * hkv * sizeof(uint32_t));
+    w.partial_m = w.partial_o + align256(rows * sinkattn::kHeadDim * sizeof(float));
+    w.partial_d = w.partial_m + align256(rows * sizeof(float));
+    w.total = w.partial_d + align256(rows * sizeof(float));
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,64 +389,24 @@ sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_t
                                       const sinkattn_tensor* partial_d, void* stream) {
     g_last_error.clear();
     SA_TRY(check_desc(q, "q", 3));
-    SA_TRY(check_desc(k, "k", 4));
-    SA_TRY(check_desc(v, "v", 4));
     SA_TRY(check_desc(partial_o, "partial_o", 4));
     SA_TRY(check_desc(partial_m, "partial_m", 3));
     SA_TRY(check_desc(partial_d, "partial_d", 3));
-
-    if (q->dtype != SINKATTN_BF16 && q->dtype != SINKATTN_F32)
-        return fail(SINKATTN_ERR_DTYPE, "q: dtype must be bf16 or f32");
-    SA_TRY(check_dtype(k, "k", q->dtype));
-    SA_TRY(check_dtype(v, "v", q->dtype));
+    sinkattn::DecodeSplitParams p{};
+    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, p));
     SA_TRY(check_dtype(partial_o, "partial_o", SINKATTN_F32));
     SA_TRY(check_dtype(partial_m, "partial_m", SINKATTN_F32));
     SA_TRY(check_dtype(partial_d, "partial_d", SINKATTN_F32));
-
-    const int64_t batch = q->shape[0], hq = q->shape[1], dim = q->shape[2];
-    const int64_t cap = k->shape[1], hkv = k->shape[2];
-    for (int i = 0; i < 4; ++i)
-        if (v->shape[i] != k->shape[i])
-            return fail(SINKATTN_ERR_SHAPE, "v: shape differs from k");
-    if (k->shape[0] != batch) return fail(SINKATTN_ERR_SHAPE, "k: batch differs from q");
-    if (k->shape[3] != dim) return fail(SINKATTN_ERR_SHAPE, "k: head_dim differs from q");
-    if (hkv <= 0 || hq <= 0 || hq % hkv != 0)
-        return fail(SINKATTN_ERR_SHAPE, "query heads (%lld) must be a positive multiple of KV heads (%lld)",
-                    (long long)hq, (long long)hkv);
-    if (num_chunks < 1) return fail(SINKATTN_ERR_SHAPE, "num_chunks must be >= 1 (got %d)", num_chunks);
-    const int64_t want_o[4] = {batch, hq, num_chunks, dim};
+    const int64_t want_o[4] = {q->shape[0], q->shape[1], num_chunks, q->shape[2]};
     for (int i = 0; i < 4; ++i)
         if (partial_o->shape[i] != want_o[i])
             return fail(SINKATTN_ERR_SHAPE, "partial_o: expected [B, Hq, num_chunks, D]");
     for (int i = 0; i < 3; ++i)
         if (partial_m->shape[i] != want_o[i] || partial_d->shape[i] != want_o[i])
             return fail(SINKATTN_ERR_SHAPE, "partial_m/partial_d: expected [B, Hq, num_chunks]");
-    SA_TRY(check_vec(seqlens_k, "seqlens_k", SINKATTN_I32, batch));
-    SA_TRY(check_vec(sinks, "sinks", SINKATTN_F32, hq));
-    SA_TRY(check_scale(scale));
-    if (dim != sinkattn::kHeadDim)
-        return fail(SINKATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (only 64)", (long long)dim);
-    const int64_t group = hq / hkv;
-    if (!is_pow2(group) || group > 16)
-        return fail(SINKATTN_ERR_UNSUPPORTED, "group size %lld not supported (1, 2, 4, 8 or 16)",
-                    (long long)group);
-    if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
-        return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
-    // Cache rows of one (sequence, KV head) slice are addressed with 32-bit byte offsets,
-    // including prefetches up to 512 rows past a chunk end.
-    if ((cap + 512) * k->stride[1] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
-        (cap + 512) * v->stride[1] * elem_size(v->dtype) >= (int64_t(1) << 31))
-        return fail(SINKATTN_ERR_UNSUPPORTED, "KV cache slice of one sequence exceeds 2 GiB");
-
-    SA_TRY(check_data(q, "q"));
-    SA_TRY(check_data(k, "k"));
-    SA_TRY(check_data(v, "v"));
     SA_TRY(check_data(partial_o, "partial_o"));
     SA_TRY(check_data(partial_m, "partial_m"));
     SA_TRY(check_data(partial_d, "partial_d"));
-    SA_TRY(check_rows(q, "q"));
-    SA_TRY(check_rows(k, "k"));
-    SA_TRY(check_rows(v, "v"));
     SA_TRY(check_contiguous(partial_o, "partial_o"));
     SA_TRY(check_contiguous(partial_m, "partial_m"));
     SA_TRY(check_contiguous(partial_d, "partial_d"));
@@ -370,35 +419,115 @@ sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_t
         for (int b = a + 1; b < 3; ++b) SA_TRY(check_disjoint(outs[a], onames[a], outs[b], onames[b]));
     }
 
-    if (batch == 0) return SINKATTN_OK;
-
-    sinkattn::DecodeSplitParams p{};
-    p.q = q->data;
-    p.k = k->data;
-    p.v = v->data;
-    p.sinks = static_cast<const float*>(sinks->data);
-    p.seqlens_k = static_cast<const int32_t*>(seqlens_k->data);
+    if (p.batch == 0) return SINKATTN_OK;
     p.partial_o = static_cast<float*>(partial_o->data);
     p.partial_m = static_cast<float*>(partial_m->data);
     p.partial_d = static_cast<float*>(partial_d->data);
-    p.q_stride_b = q->stride[0];
-    p.q_stride_head = q->stride[1];
-    p.k_stride_b = k->stride[0];
-    p.k_stride_tok = k->stride[1];
-    p.k_stride_head = k->stride[2];
-    p.v_stride_b = v->stride[0];
-    p.v_stride_tok = v->stride[1];
-    p.v_stride_head = v->stride[2];
-    p.capacity = cap;
-    p.chunk_size = (cap + num_chunks - 1) / num_chunks;
-    p.batch = static_cast<int32_t>(batch);
-    p.num_q_heads = static_cast<int32_t>(hq);
-    p.num_kv_heads = static_cast<int32_t>(hkv);
-    p.num_chunks = num_chunks;
-    p.scale = scale;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_decode_split_bf16(p, s)
                                               : sinkattn::launch_decode_split_f32(p, s));
+}
+
+sinkattn_status sinkattn_decode(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                void* workspace, size_t workspace_bytes,
+                                const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(q, "q", 3));
+    SA_TRY(check_desc(out, "out", 3));
+    if (lse != nullptr) SA_TRY(check_desc(lse, "lse", 2));
+    sinkattn::DecodeSplitParams p{};
+    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, p));
+    if (q->dtype == SINKATTN_F32) SA_TRY(check_dtype(out, "out", SINKATTN_F32));
+    else if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
+    if (lse != nullptr) SA_TRY(check_dtype(lse, "lse", SINKATTN_F32));
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i]) return fail(SINKATTN_ERR_SHAPE, "out: expected [B, Hq, D]");
+    if (lse != nullptr && (lse->shape[0] != q->shape[0] || lse->shape[1] != q->shape[1]))
+        return fail(SINKATTN_ERR_SHAPE, "lse: expected [B, Hq]");
+    const WorkspaceLayout w = workspace_layout(p.batch, p.num_q_heads, p.num_kv_heads, num_chunks);
+    if (workspace_bytes < w.total)
+        return fail(SINKATTN_ERR_SHAPE, "workspace: %zu bytes, need %zu", workspace_bytes, w.total);
+    if (w.total > 0 && workspace == nullptr) return fail(SINKATTN_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(SINKATTN_ERR_LAYOUT, "workspace not 256-byte aligned");
+    SA_TRY(check_data(out, "out"));
+    SA_TRY(check_rows(out, "out"));
+    SA_TRY(check_no_self_overlap(out, "out"));
+    if (lse != nullptr) {
+        SA_TRY(check_data(lse, "lse"));
+        if (reinterpret_cast<uintptr_t>(lse->data) % 4 != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "lse: data pointer not 4-byte aligned");
+        if (lse->stride[1] != 1 && lse->shape[1] > 1)
+            return fail(SINKATTN_ERR_LAYOUT, "lse: innermost stride must be 1");
+        SA_TRY(check_no_self_overlap(lse, "lse"));
+    }
+    // The workspace is written too: it may not overlap any tensor argument.
+    sinkattn_tensor ws{};
+    ws.data = workspace;
+    ws.dtype = SINKATTN_F32;
+    ws.ndim = 1;
+    ws.shape[0] = static_cast<int64_t>(w.total / 4);
+    ws.stride[0] = 1;
+    const sinkattn_tensor* ins[5] = {q, k, v, sinks, seqlens_k};
+    const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
+    for (int b = 0; b < 5; ++b) {
+        SA_TRY(check_disjoint(out, "out", ins[b], inames[b]));
+        SA_TRY(check_disjoint(&ws, "workspace", ins[b], inames[b]));
+        if (lse != nullptr) SA_TRY(check_disjoint(lse, "lse", ins[b], inames[b]));
+    }
+    SA_TRY(check_disjoint(out, "out", &ws, "workspace"));
+    if (lse != nullptr) {
+        SA_TRY(check_disjoint(lse, "lse", &ws, "workspace"));
+        SA_TRY(check_disjoint(out, "out", lse, "lse"));
+    }
+
+    if (p.batch == 0) return SINKATTN_OK;
+    char* base = static_cast<char*>(workspace);
+    p.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+    p.partial_o = reinterpret_cast<float*>(base + w.partial_o);
+    p.partial_m = reinterpret_cast<float*>(base + w.partial_m);
+    p.partial_d = reinterpret_cast<float*>(base + w.partial_d);
+    p.out = out->data;
+    p.lse = lse != nullptr ? static_cast<float*>(lse->data) : nullptr;
+    p.o_stride_b = out->stride[0];
+    p.o_stride_head = out->stride[1];
+    p.lse_stride_b = lse != nullptr ? lse->stride[0] : 0;
+    p.lse_stride_head = lse != nullptr ? lse->stride[1] : 0;
+    p.out_is_bf16 = out->dtype == SINKATTN_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (q->dtype == SINKATTN_BF16) return launched(sinkattn::launch_decode_fused_bf16(p, s));
+    // fp32 reference variant: the two-kernel path through the same workspace.
+    SA_TRY(launched(sinkattn::launch_decode_split_f32(p, s)));
+    sinkattn::DecodeMergeParams mp{};
+    mp.partial_o = p.partial_o;
+    mp.partial_m = p.partial_m;
+    mp.partial_d = p.partial_d;
+    mp.out = p.out;
+    mp.lse = p.lse;
+    mp.o_stride_b = p.o_stride_b;
+    mp.o_stride_head = p.o_stride_head;
+    mp.lse_stride_b = p.lse_stride_b;
+    mp.lse_stride_head = p.lse_stride_head;
+    mp.batch = p.batch;
+    mp.num_q_heads = p.num_q_heads;
+    mp.num_chunks = num_chunks;
+    mp.out_is_bf16 = p.out_is_bf16;
+    return launched(sinkattn::launch_decode_merge(mp, s));
+}
+
+size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
+                                      int num_chunks) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_chunks < 1) return 0;
+    return workspace_layout(batch, num_q_heads, num_kv_heads, num_chunks).total;
+}
+
+size_t sinkattn_decode_workspace_counter_bytes(int64_t batch, int64_t num_kv_heads) {
+    if (batch < 0 || num_kv_heads <= 0) return 0;
+    return align256(static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t));
 }
 
 sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,

@@ -139,9 +139,10 @@ __device__ __forceinline__ void fold_block(SplitState& st, const KvBlock& r, con
 // kHeads KV heads per work-group, four waves each. With two, the work-group reads both
 // heads' 128-byte slices of every cache row together (256 contiguous bytes of a token-major
 // row), which the memory system serves measurably faster than lone 128-byte slices.
-template <int kHeads>
+template <int kHeads, bool kFused>
 __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kernel(DecodeSplitParams p) {
     constexpr int kWaves = kSplitWaves * kHeads;
+    __shared__ int last_arrival;
     __shared__ __attribute__((aligned(16))) __bf16 v_tile[kWaves][kBlockKeys][kVPitch];
     __shared__ __attribute__((aligned(16))) float red_m[kWaves][16];
     __shared__ __attribute__((aligned(16))) float red_d[kWaves][16];
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     // cache rows are dispatched together.
     int bid = blockIdx.x;
     const int heads_per_row = p.num_kv_heads / kHeads;
-    const int g = (bid % heads_per_row) * kHeads + hsub;
+    const int head_set = bid % heads_per_row;  // this work-group's KV heads: kHeads * head_set + ...
+    const int g = head_set * kHeads + hsub;
     bid /= heads_per_row;
     const int chunk = bid % p.num_chunks;
     const int b = bid / p.num_chunks;
@@ -257,6 +259,49 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
             p.partial_d[row] = wsum;
         }
     }
+
+    if constexpr (kFused) {
+        // Publish this chunk's states, then count the work-group done for its (sequence, KV
+        // heads). The device-scope fences write back / invalidate the per-XCD L2 caches, so the
+        // last work-group reads every chunk's states whichever XCD produced them.
+        __threadfence();
+        __syncthreads();
+        uint32_t* counter = p.counters + static_cast<int64_t>(b) * heads_per_row + head_set;
+        if (threadIdx.x == 0)
+            last_arrival = atomicAdd(counter, 1u) == static_cast<uint32_t>(p.num_chunks - 1);
+        __syncthreads();
+        if (!last_arrival) return;
+        __threadfence();
+        // Log-sum-exp merge of all chunks for this work-group's kHeads * G query heads.
+        const int first_head = head_set * kHeads * group;
+        for (int idx = threadIdx.x; idx < kHeads * group * kHeadDim; idx += kSplitThreads * kHeads) {
+            const int h = first_head + idx / kHeadDim;
+            const int d = idx % kHeadDim;
+            const int64_t row0 = (static_cast<int64_t>(b) * p.num_q_heads + h) * p.num_chunks;
+            float big = kNegInf;
+            for (int c = 0; c < p.num_chunks; ++c) big = fmaxf(big, p.partial_m[row0 + c]);
+            float wsum = 0.0f, osum = 0.0f;
+            if (big != kNegInf) {
+                for (int c = 0; c < p.num_chunks; ++c) {
+                    const float mc = p.partial_m[row0 + c];
+                    if (mc == kNegInf) continue;
+                    const float w = p.partial_d[row0 + c] * expf(mc - big);
+                    wsum += w;
+                    osum = fmaf(w, p.partial_o[(row0 + c) * kHeadDim + d], osum);
+                }
+            }
+            const float o = wsum > 0.0f ? osum / wsum : 0.0f;
+            const int64_t off = b * p.o_stride_b + h * p.o_stride_head + d;
+            if (p.out_is_bf16)
+                static_cast<__bf16*>(p.out)[off] = (__bf16)o;
+            else
+                static_cast<float*>(p.out)[off] = o;
+            if (p.lse != nullptr && d == 0)
+                p.lse[b * p.lse_stride_b + h * p.lse_stride_head] = wsum > 0.0f ? big + logf(wsum) : kNegInf;
+        }
+        // Leave the counter at zero for the next call.
+        if (threadIdx.x == 0) atomicExch(counter, 0u);
+    }
 }
 
 // fp32 reference variant: one thread per (b, query head, chunk), keys visited one at a time with
@@ -317,20 +362,30 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(DecodeSplitParams
 // Compute units of an MI355X / MI350X (gfx950).
 constexpr int64_t kComputeUnits = 256;
 
-hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream) {
+template <bool kFused>
+hipError_t launch_split(const DecodeSplitParams& p, hipStream_t stream) {
     // Pair two KV heads per work-group only where their slices of a cache row are adjacent
     // (token-major caches) and the paired grid still gives every compute unit a work-group;
     // head-major caches already stream contiguous rows and prefer the finer grid.
     const bool adjacent = p.k_stride_head == kHeadDim && p.v_stride_head == kHeadDim;
     const int64_t paired_groups = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 2) * p.num_chunks;
     if (p.num_kv_heads % 2 == 0 && adjacent && paired_groups >= kComputeUnits) {
-        const int64_t blocks = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 2) * p.num_chunks;
-        decode_split_bf16_kernel<2><<<dim3(static_cast<unsigned>(blocks)), dim3(2 * kSplitThreads), 0, stream>>>(p);
+        decode_split_bf16_kernel<2, kFused>
+            <<<dim3(static_cast<unsigned>(paired_groups)), dim3(2 * kSplitThreads), 0, stream>>>(p);
     } else {
         const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_chunks;
-        decode_split_bf16_kernel<1><<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitThreads), 0, stream>>>(p);
+        decode_split_bf16_kernel<1, kFused>
+            <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitThreads), 0, stream>>>(p);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream) {
+    return launch_split<false>(p, stream);
+}
+
+hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stream) {
+    return launch_split<true>(p, stream);
 }
 
 hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t stream) {

@@ -52,6 +52,14 @@ struct DecodeSplitParams {
     int32_t num_kv_heads;
     int32_t num_chunks;
     float scale;
+    // Fused split + merge only (sinkattn_decode): zero-initialised completion counters, one per
+    // (sequence, KV head), and the merged outputs.
+    uint32_t* counters;
+    void* out;
+    float* lse;          // may be null
+    int64_t o_stride_b, o_stride_head;
+    int64_t lse_stride_b, lse_stride_head;
+    int32_t out_is_bf16;
 };
 
 struct DecodeMergeParams {
@@ -72,6 +80,8 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream);
 hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t stream);
+// Split and merge in one launch (bf16); partials and counters as in DecodeSplitParams.
+hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream);
 
 }  // namespace sinkattn

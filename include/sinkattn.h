@@ -42,13 +42,14 @@
 #ifndef SINKATTN_H
 #define SINKATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define SINKATTN_VERSION 1
+#define SINKATTN_VERSION 2
 
 typedef enum {
     SINKATTN_OK = 0,
@@ -96,7 +97,7 @@ typedef struct {
  *
  * A row that sees no key returns 0 (all weight sits on the value-less sink; with sink = -inf the
  * 0/0 row is defined as 0). Tq = 0 or B = 0 launches nothing and returns SINKATTN_OK.
- * Supported group sizes Hq/Hkv: powers of two up to 64.
+ * Supported group sizes Hq/Hkv: powers of two up to 128.
  */
 sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
                                  const sinkattn_tensor* v, const sinkattn_tensor* sinks,
@@ -162,6 +163,43 @@ sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
                                       const sinkattn_tensor* partial_d, int num_chunks,
                                       const sinkattn_tensor* out, const sinkattn_tensor* lse,
                                       void* stream);
+
+/*
+ * sinkattn_decode - split-KV decode and its log-sum-exp merge in one launch.
+ *
+ * Same computation and inputs as sinkattn_decode_split followed by sinkattn_decode_merge ("GPT-OSS
+ * on Day 0", "Sink attention" subsection: split along the KV length, sink in the first chunk only,
+ * chunks combined), without the second launch: every work-group writes its chunk states into
+ * `workspace`, counts itself done on a per-(sequence, KV-head group) counter, and the last one
+ * to finish merges that group's chunks and writes `out` (and `lse`).
+ *
+ *   q, k, v, sinks, seqlens_k, num_chunks, scale: as for sinkattn_decode_split
+ *   workspace       device memory, 256-byte aligned, at least
+ *                   sinkattn_decode_workspace_size(B, Hq, Hkv, num_chunks) bytes. Its counter
+ *                   region (the first sinkattn_decode_workspace_counter_bytes(B, Hkv) bytes) must
+ *                   be zero before the first call (e.g. one hipMemsetAsync after allocating);
+ *                   every call that runs to completion leaves it zero again, so a workspace can be
+ *                   reused, also by calls replayed from a HIP graph. Calls sharing a workspace must
+ *                   not overlap in time.
+ *   workspace_bytes size of that memory
+ *   out             [B, Hq, D] bf16 | fp32 (fp32 only if q is fp32)
+ *   lse             [B, Hq] fp32 (natural log of each row's softmax denominator) or NULL
+ *
+ * Supported group sizes Hq/Hkv: 1, 2, 4, 8, 16. B = 0 launches nothing.
+ */
+sinkattn_status sinkattn_decode(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                void* workspace, size_t workspace_bytes,
+                                const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                void* stream);
+
+/* Bytes of workspace sinkattn_decode needs (0 for invalid arguments). */
+size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
+                                      int num_chunks);
+
+/* Bytes at the start of that workspace holding the counters that must start at zero. */
+size_t sinkattn_decode_workspace_counter_bytes(int64_t batch, int64_t num_kv_heads);
 
 /* Short static description of a status code. Never NULL. */
 const char* sinkattn_status_string(sinkattn_status status);

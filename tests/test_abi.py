@@ -51,7 +51,7 @@ def last_error():
 # ----------------------------------------------------------------------------- exports
 def test_every_declared_function_is_exported():
     text = open(HEADER).read()
-    names = set(re.findall(r"^\s*(?:const\s+char\s*\*|sinkattn_status|int)\s+(sinkattn_\w+)\s*\(",
+    names = set(re.findall(r"^\s*(?:const\s+char\s*\*|sinkattn_status|int|size_t)\s+(sinkattn_\w+)\s*\(",
                            text, flags=re.M))
     assert {"sinkattn_prefill", "sinkattn_decode_split", "sinkattn_decode_merge"} <= names
     for name in names:
@@ -234,3 +234,59 @@ def test_error_message_is_cleared_by_next_call():
     assert last_error()
     assert call_merge(merge_args(b=0)) == _lib.OK
     assert last_error() == ""
+
+
+# ----------------------------------------------------------------------------- fused decode
+def fused_args(b=2, hq=8, hkv=1, cap=64, chunks=4, dim=64, dtype=BF16, lse=True):
+    a = dict(q=T([b, hq, dim], dtype), k=T([b, cap, hkv, dim], dtype), v=T([b, cap, hkv, dim], dtype),
+             sinks=T([hq], F32), seqlens=T([b], I32), chunks=chunks, scale=0.125,
+             out=T([b, hq, dim], dtype), lse=T([b, hq], F32) if lse else None)
+    a["ws_bytes"] = _lib.lib.sinkattn_decode_workspace_size(b, hq, hkv, chunks)
+    a["ws"] = T([max(1, a["ws_bytes"] // 4)], F32).data
+    return a
+
+
+def call_fused(a):
+    return _lib.lib.sinkattn_decode(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]), R(a["seqlens"]),
+                                    a["chunks"], a["scale"], a["ws"], a["ws_bytes"], R(a["out"]),
+                                    R(a["lse"]), None)
+
+
+def test_workspace_size_formula():
+    # counters (B*Hkv u32) + partial_o + partial_m + partial_d, each rounded up to 256 bytes
+    def up(x):
+        return (x + 255) // 256 * 256
+    for b, hq, hkv, c in [(8, 64, 8, 8), (1, 4, 1, 4), (3, 12, 3, 5), (0, 64, 8, 8)]:
+        rows = b * hq * c
+        want = up(b * hkv * 4) + up(rows * 64 * 4) + 2 * up(rows * 4)
+        assert _lib.lib.sinkattn_decode_workspace_size(b, hq, hkv, c) == want
+        assert _lib.lib.sinkattn_decode_workspace_counter_bytes(b, hkv) == up(b * hkv * 4)
+    assert _lib.lib.sinkattn_decode_workspace_size(2, 8, 1, 0) == 0
+    assert _lib.lib.sinkattn_decode_workspace_size(2, 8, 0, 4) == 0
+
+
+def test_fused_empty_batch_is_ok():
+    assert call_fused(fused_args(b=0)) == _lib.OK
+
+
+FUSED_CASES = [
+    ("ws_null", lambda a: _mut(a, ws=None), _lib.ERR_NULL),
+    ("ws_small", lambda a: _mut(a, ws_bytes=a["ws_bytes"] - 4), _lib.ERR_SHAPE),
+    ("ws_misaligned", lambda a: _mut(a, ws=a["ws"] + 64), _lib.ERR_LAYOUT),
+    ("ws_overlaps_k", lambda a: _mut(a, ws=a["k"].data), _lib.ERR_LAYOUT),
+    ("out_overlaps_ws", lambda a: _mut(a, out=T([2, 8, 64], addr=a["ws"] + 256)), _lib.ERR_LAYOUT),
+    ("out_shape", lambda a: _mut(a, out=T([2, 4, 64])), _lib.ERR_SHAPE),
+    ("out_int", lambda a: _mut(a, out=T([2, 8, 64], I32)), _lib.ERR_DTYPE),
+    ("lse_shape", lambda a: _mut(a, lse=T([2, 4], F32)), _lib.ERR_SHAPE),
+    ("lse_overlaps_out", lambda a: _mut(a, lse=T([2, 8], F32, addr=a["out"].data)), _lib.ERR_LAYOUT),
+    ("chunks_zero", lambda a: _mut(a, chunks=0), _lib.ERR_SHAPE),
+    ("group_32", lambda a: fused_args(hq=32), _lib.ERR_UNSUPPORTED),
+    ("f32_in_bf16_out", lambda a: _mut(fused_args(dtype=F32), out=T([2, 8, 64], BF16)), _lib.ERR_DTYPE),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_rejects(name, mutate, code):
+    status = call_fused(mutate(fused_args()))
+    assert status == code, (status, last_error())
+    assert last_error()

@@ -362,3 +362,96 @@ def test_graph_replays_match_eager():
         work()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, eager_dec)
+
+
+# ----------------------------------------------------------------------------- fused split + merge
+FUSED_CASES = [c for c in DECODE_SMALL if c[0] in
+               ("uniform", "ragged_empty_chunks", "many_chunks", "group16", "outliers", "odd_kv_heads",
+                "single_kv_head", "paired_heads", "kv_len_1", "weak_sinks")]
+
+
+@pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,sr,op", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_decode_fused_bf16(name, lens, cap, chunks, hq, hkv, sr, op):
+    sa = _sa()
+    case = workloads.make_decode(lens, cap, chunks, num_q_heads=hq, num_kv_heads=hkv, sink_range=sr,
+                                 outlier_p=op, seed=_seed(name), poison=True)
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    ws = sa.decode_workspace(len(lens), hq, hkv, chunks, "cuda")
+    ref, rlse = oracle_decode(case)
+    for call in range(2):  # the second call reuses the workspace the first left behind
+        out, lse = sa.decode_fused(q, k, v, sinks, sl, chunks, case.scale, ws, return_lse=True)
+        torch.cuda.synchronize()
+        check_bf16(out, ref, f"fused {name} call {call}")
+        g = _np(lse)
+        assert np.array_equal(np.isneginf(g), np.isneginf(rlse))
+        fin = np.isfinite(rlse)
+        np.testing.assert_allclose(g[fin], rlse[fin], atol=1e-3)
+    counter_bytes = sa._lib.lib.sinkattn_decode_workspace_counter_bytes(len(lens), hkv)
+    assert torch.count_nonzero(ws[:counter_bytes]).item() == 0, "counters not reset"
+
+
+def test_decode_fused_workspace_reuse_with_smaller_problem():
+    """A workspace sized for a large call serves a smaller, different call next."""
+    sa = _sa()
+    big = workloads.make_decode([900, 1024, 5, 700, 1, 0, 333, 1000], 1024, 8, seed=31, poison=True)
+    small = workloads.make_decode([77, 3], 128, 4, num_q_heads=16, num_kv_heads=2, seed=32, poison=True)
+    ws = sa.decode_workspace(8, 64, 8, 8, "cuda")
+    for case in (big, small, big):
+        q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+        out = sa.decode_fused(q, k, v, sinks, sl, case.num_chunks, case.scale, ws)
+        torch.cuda.synchronize()
+        ref, _ = oracle_decode(case)
+        check_bf16(out, ref, f"fused reuse B={case.q.shape[0]}")
+    assert torch.count_nonzero(ws[:sa._lib.lib.sinkattn_decode_workspace_counter_bytes(8, 8)]).item() == 0
+
+
+def test_decode_fused_fp32_tiny():
+    sa = _sa()
+    w = workloads.make(1)
+    case = w.decode
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    ws = sa.decode_workspace(1, 4, 1, 4, "cuda")
+    out, lse = sa.decode_fused(q, k, v, sinks, sl, 4, case.scale, ws, return_lse=True)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_decode(case)
+    check_f32(out, ref, "fused tiny f32")
+    np.testing.assert_allclose(_np(lse), rlse, rtol=1e-5)
+
+
+def test_full_decode_workload_2_fused():
+    sa = _sa()
+    case = workloads.make(2, poison=True).decode
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    ws = sa.decode_workspace(8, 64, 8, 8, "cuda")
+    out = sa.decode_fused(q, k, v, sinks, sl, 8, case.scale, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode(case)
+    check_bf16(out, ref, "workload 2 fused decode")
+
+
+def test_graph_replays_fused_decode():
+    sa = _sa()
+    dec = workloads.make_decode([700, 33, 1024, 0] * 16, 1024, 8, seed=41)  # paired kernel (64*4*8 >= 256)
+    q, k, v, s, sl = _dev(dec.q, dec.k, dec.v, dec.sinks, dec.seqlens_k)
+    ws = sa.decode_workspace(64, 64, 8, 8, "cuda")
+    out = torch.empty((64, 64, 64), dtype=torch.bfloat16, device="cuda")
+    sa.decode_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sa.decode_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sa.decode_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
+    for rep in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+        sa.decode_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)

@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the sink-attention hot path on one MI355X.
 
-One step = one split-KV decode (sinkattn_decode_split + sinkattn_decode_merge) of the decode
-workload: 8 sequences x 8192 cached tokens, 64 query heads over 8 KV heads, head_dim 64, bf16,
-8 chunks of 1024 keys. ``value`` is algorithmic KV bytes per second (the K and V rows actually
+One step = one split-KV decode of the decode workload (sinkattn_decode_split then
+sinkattn_decode_merge): 8 sequences x 8192 cached tokens, 64 query heads over 8 KV heads,
+head_dim 64, bf16, 8 chunks of 1024 keys. The single-launch form (sinkattn_decode: chunk states
+and their merge in one kernel) is timed beside it. ``value`` is algorithmic KV bytes per second (the K and V rows actually
 read plus q, out and sinks), with inputs resident in HBM. Decode inputs rotate over enough copies
 (> 512 MB in all) that the 256 MB Infinity Cache cannot serve a step from the previous one.
 
@@ -38,7 +39,7 @@ CALIB_BYTES = 256 * 2**20
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_b8_len8192_pmc.txt")
 # The split kernel's complete source: its traffic figure is only reused while these are unchanged.
 SPLIT_SOURCES = [os.path.join(ROOT, "gqa_learned_softmax_amd", "csrc", f)
-                 for f in ("decode_split.hip", "device_common.h", "launch.h")]
+                 for f in ("decode_split.hip", "chunk_merge.h", "device_common.h", "launch.h")]
 
 
 def _log(msg):
@@ -185,6 +186,10 @@ def main():
     pm = torch.empty((batch, hq, chunks), dtype=torch.float32, device=dev)
     pd = torch.empty((batch, hq, chunks), dtype=torch.float32, device=dev)
     out = torch.empty((batch, hq, dim), dtype=torch.bfloat16, device=dev)
+    ws = sa.decode_workspace(batch, hq, case.k.shape[2], chunks, dev)
+
+    def fused(i):
+        sa.decode_fused(q, ks[i % n_sets], vs[i % n_sets], sinks, seqlens, chunks, case.scale, ws, out=out)
 
     def split(i):
         sa.decode_split(q, ks[i % n_sets], vs[i % n_sets], sinks, seqlens, chunks, case.scale, po, pm, pd)
@@ -192,9 +197,11 @@ def main():
     def merge(i):
         sa.decode_merge(po, pm, pd, out=out)
 
-    def step(i):
+    def split_merge(i):
         split(i)
         merge(i)
+
+    step = split_merge
 
     def step_hot(i):
         sa.decode_split(q, k0, v0, sinks, seqlens, chunks, case.scale, po, pm, pd)
@@ -219,8 +226,10 @@ def main():
     ms_step = start.elapsed_time(end) / args.steps
     _log(f"decode step {ms_step * 1e3:.2f} us ({wall * 1e3:.2f} ms wall for {args.steps} steps)")
     n_rep = max(args.steps, 50)
+    ms_fused = _time_graph(_capture(fused, n_rep, torch), n_rep, torch)
     ms_split = _time_graph(_capture(split, n_rep, torch), n_rep, torch)
     ms_merge = _time_graph(_capture(merge, n_rep, torch), n_rep, torch)
+    ms_two = _time_graph(_capture(split_merge, n_rep, torch), n_rep, torch)
     ms_hot = _time_graph(_capture(step_hot, n_rep, torch), n_rep, torch) if args.hot else None
     ms_eager = None
     torch.cuda.synchronize()
@@ -233,8 +242,10 @@ def main():
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / n_rep
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    fused_gbs = step_bytes / (ms_fused * 1e-3) / 1e9
     split_gbs = split_bytes / (ms_split * 1e-3) / 1e9
-    _log(f"split {ms_split * 1e3:.2f} us ({split_gbs:.0f} GB/s), merge {ms_merge * 1e3:.2f} us"
+    _log(f"split {ms_split * 1e3:.2f} us ({split_gbs:.0f} GB/s), merge {ms_merge * 1e3:.2f} us, "
+         f"split+merge {ms_two * 1e3:.2f} us; fused {ms_fused * 1e3:.2f} us ({fused_gbs:.0f} GB/s)"
          + (f", hot step {ms_hot * 1e3:.2f} us" if ms_hot else ""))
 
     traffic = _traffic_from_profile(_source_hash(SPLIT_SOURCES))
@@ -259,7 +270,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_bf16",
+            "kernel": "decode_split_bf16_kernel<2, false>",
             "achieved": round(split_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -270,6 +281,9 @@ def main():
         },
         "decode_detail": {
             "split_us": round(ms_split * 1e3, 3), "merge_us": round(ms_merge * 1e3, 3),
+            "split_plus_merge_us": round(ms_two * 1e3, 3),
+            "fused_sinkattn_decode_us": round(ms_fused * 1e3, 3),
+            "fused_gbs": round(fused_gbs, 2),
             "step_us_rotated": round(ms_step * 1e3, 3),
             "step_us_hot": round(ms_hot * 1e3, 3) if ms_hot else None,
             "step_us_eager_python_launch": round(ms_eager * 1e3, 3),

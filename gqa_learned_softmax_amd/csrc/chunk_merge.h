@@ -1,0 +1,71 @@
+// Log-sum-exp combination of split-KV chunk states, one wave per (sequence, query head).
+//
+// Source: the split along the KV length in "GPT-OSS on Day 0" (Perplexity), section "Kernels for
+// GPT-OSS", subsection "Sink attention", needs the per-chunk softmax states to be combined; the
+// page names the split and the rule that only the first chunk carries the sink, and this is the
+// standard combination of (max, scale, normalised output) states:
+//   M = max_c m_c, w_c = d_c e^(m_c - M), out = sum_c w_c o_c / sum_c w_c, lse = M + ln sum_c w_c.
+// Used by the stand-alone merge kernel and by the last work-group of the fused decode kernel.
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace sinkattn {
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Combines `chunks` states of one row: pm/pd hold (m_c, d_c) (natural-log m), po holds the
+// normalised chunk outputs o_c as `chunks` rows of kHeadDim floats. Lane d of the calling wave
+// receives out[d]; `lse` is the same in every lane. Chunks are taken 64 at a time: lane c loads
+// (m_c, d_c), the wave agrees on the maximum, each lane forms its weight w_c, and lane d then
+// accumulates w_c * o_c[d] with w_c broadcast from lane c (v_readlane). The loads of a block are
+// independent of each other, so they are in flight together; with at most 64 chunks the states
+// are loaded once.
+__device__ __forceinline__ void merge_chunk_states(const float* pm, const float* pd, const float* po,
+                                                   int chunks, int lane, float& out, float& lse) {
+    const float m_first = lane < chunks ? pm[lane] : kNegInf;
+    const float d_first = lane < chunks ? pd[lane] : 0.0f;
+    float big = m_first;
+    for (int c = 64 + lane; c - lane < chunks; c += 64) big = fmaxf(big, c < chunks ? pm[c] : kNegInf);
+    big = wave_max(big);
+    float wsum = 0.0f, osum = 0.0f;
+    if (big != kNegInf) {
+        for (int c0 = 0; c0 < chunks; c0 += 64) {
+            const int c = c0 + lane;
+            const float mc = c0 == 0 ? m_first : (c < chunks ? pm[c] : kNegInf);
+            const float dc = c0 == 0 ? d_first : (c < chunks ? pd[c] : 0.0f);
+            const float w = mc == kNegInf ? 0.0f : dc * expf(mc - big);
+            wsum += w;
+            const int n = chunks - c0 < 64 ? chunks - c0 : 64;
+            const float* rows = po + static_cast<int64_t>(c0) * kHeadDim + lane;
+            int j = 0;
+            for (; j + 8 <= n; j += 8) {
+                float o[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) o[u] = rows[static_cast<int64_t>(j + u) * kHeadDim];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    osum = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u)), o[u], osum);
+            }
+            for (; j < n; ++j)
+                osum = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)),
+                            rows[static_cast<int64_t>(j) * kHeadDim], osum);
+        }
+        wsum = wave_sum(wsum);
+    }
+    out = wsum > 0.0f ? osum / wsum : 0.0f;
+    lse = wsum > 0.0f ? big + logf(wsum) : kNegInf;
+}
+
+}  // namespace sinkattn

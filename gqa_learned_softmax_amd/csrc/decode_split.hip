@@ -20,6 +20,7 @@
 //     wave-private LDS tile (128-bit writes) and comes back transposed through the gfx950
 //     transpose read, so no element-wise transposition is needed.
 
+#include "chunk_merge.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -262,42 +263,34 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
 
     if constexpr (kFused) {
         // Publish this chunk's states, then count the work-group done for its (sequence, KV
-        // heads). The device-scope fences write back / invalidate the per-XCD L2 caches, so the
-        // last work-group reads every chunk's states whichever XCD produced them.
-        __threadfence();
+        // heads). The barrier orders every wave's stores before thread 0's device-scope release
+        // fence (an L2 write-back); only the last arrival takes the acquire fence (an L2 and L1
+        // invalidate), after which it reads every chunk's states whichever XCD produced them.
         __syncthreads();
         uint32_t* counter = p.counters + static_cast<int64_t>(b) * heads_per_row + head_set;
-        if (threadIdx.x == 0)
-            last_arrival = atomicAdd(counter, 1u) == static_cast<uint32_t>(p.num_chunks - 1);
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const bool last = atomicAdd(counter, 1u) == static_cast<uint32_t>(p.num_chunks - 1);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            last_arrival = last;
+        }
         __syncthreads();
         if (!last_arrival) return;
-        __threadfence();
-        // Log-sum-exp merge of all chunks for this work-group's kHeads * G query heads.
-        const int first_head = head_set * kHeads * group;
-        for (int idx = threadIdx.x; idx < kHeads * group * kHeadDim; idx += kSplitThreads * kHeads) {
-            const int h = first_head + idx / kHeadDim;
-            const int d = idx % kHeadDim;
-            const int64_t row0 = (static_cast<int64_t>(b) * p.num_q_heads + h) * p.num_chunks;
-            float big = kNegInf;
-            for (int c = 0; c < p.num_chunks; ++c) big = fmaxf(big, p.partial_m[row0 + c]);
-            float wsum = 0.0f, osum = 0.0f;
-            if (big != kNegInf) {
-                for (int c = 0; c < p.num_chunks; ++c) {
-                    const float mc = p.partial_m[row0 + c];
-                    if (mc == kNegInf) continue;
-                    const float w = p.partial_d[row0 + c] * expf(mc - big);
-                    wsum += w;
-                    osum = fmaf(w, p.partial_o[(row0 + c) * kHeadDim + d], osum);
-                }
-            }
-            const float o = wsum > 0.0f ? osum / wsum : 0.0f;
-            const int64_t off = b * p.o_stride_b + h * p.o_stride_head + d;
+        // Log-sum-exp merge of all chunks for this work-group's kHeads * G query heads, one wave
+        // per head at a time.
+        const int lane = threadIdx.x & 63;
+        for (int hl = wave_all; hl < kHeads * group; hl += kWaves) {
+            const int h = head_set * kHeads * group + hl;
+            const int64_t bh = static_cast<int64_t>(b) * p.num_q_heads + h;
+            float o, lse;
+            merge_chunk_states(p.partial_m + bh * p.num_chunks, p.partial_d + bh * p.num_chunks,
+                               p.partial_o + bh * p.num_chunks * kHeadDim, p.num_chunks, lane, o, lse);
+            const int64_t off = b * p.o_stride_b + h * p.o_stride_head + lane;
             if (p.out_is_bf16)
                 static_cast<__bf16*>(p.out)[off] = (__bf16)o;
             else
                 static_cast<float*>(p.out)[off] = o;
-            if (p.lse != nullptr && d == 0)
-                p.lse[b * p.lse_stride_b + h * p.lse_stride_head] = wsum > 0.0f ? big + logf(wsum) : kNegInf;
+            if (p.lse != nullptr && lane == 0) p.lse[b * p.lse_stride_b + h * p.lse_stride_head] = lse;
         }
         // Leave the counter at zero for the next call.
         if (threadIdx.x == 0) atomicExch(counter, 0u);

@@ -13,9 +13,12 @@
 // Per 64-key tile, per wave (32 v_mfma_f32_32x32x16_bf16, the gfx950 shape with the highest
 // sustained rate):
 //   S^T (64 keys x 64 rows) = K (LDS, row-major) . Q^T (registers): 16 MFMA.
-//   online softmax per row in the log2 domain (scale and sink pre-multiplied by log2 e), one FMA
-//     per score for scale-and-subtract, lazy rescaling, causal mask only on tiles that cross
-//     the diagonal or the sequence end.
+//   online softmax per row in the log2 domain (scale and sink multiplied by log2 e in fp32).
+//     Causal mask only on the tiles that cross the diagonal or the sequence end, which come
+//     last and run in a loop of their own.
+//   On tiles where the softmax needs no row max (zero reference, below), the MFMA chains and
+//   the exponentials are interleaved by hand so that the wave keeps its matrix and vector
+//   pipes busy together.
 //   O^T (64 d x 64 rows) += V^T . P^T: 16 MFMA. The S^T accumulator lanes are exactly the P^T
 //     operand lanes, so P never leaves registers; V stays row-major in LDS and comes back
 //     transposed through ds_read_b64_tr_b16.
@@ -25,6 +28,8 @@
 // work-groups (which the dispatcher spreads over the eight XCDs) read different KV heads and each
 // XCD's L2 keeps re-serving one head's K/V. Within a sequence, tiles are issued last-position
 // first: the longest causal rows start earliest.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -42,10 +47,20 @@ constexpr int kKeyTile = 64;
 // transpose read land on disjoint bank ranges.
 constexpr int kKPitch = 72;
 constexpr int kVPitch = 96;
-// Lazy rescaling: the running max is only raised (and the accumulators rescaled) when a tile's
-// max exceeds it by more than this many log2 units; in between, exp2(s - m) <= 2^8 stays exact
-// enough in fp32 and bf16 and the division by d at the end cancels the stale max.
+// Softmax reference. Each row keeps a reference m; p = exp2(s - m) and d, O are kept relative
+// to it, so any m that keeps p away from fp32/bf16 overflow and underflow gives the same
+// out = O / d (the common factor 2^-m cancels). Two regimes:
+//  * running-max tiles: m is the running max, raised (and O, d rescaled) only when a tile's max
+//    exceeds it by more than kRescaleSlack log2 units, so p <= 2^8;
+//  * zero-reference tiles: once the running max of a row lies in [-kZeroRefLimit, kZeroRefLimit]
+//    the row is rescaled once to m = 0, and while every row of a wave has m = 0 its tiles need
+//    neither a row max nor a subtraction: p = exp2(s). The row's largest contribution so far is
+//    then at least 2^-kZeroRefLimit, so nothing that matters can underflow; overflow is checked
+//    once at the end: a work-group in which any row's d exceeds kFastSumLimit (every p is at
+//    most d) or any d or O is not finite is recomputed with running-max tiles only.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kZeroRefLimit = 16.0f;
+constexpr float kFastSumLimit = 18446744073709551616.0f;  // 2^64
 
 // Maps a linear query-tile index to (sequence, first position). Tiles are numbered sequence by
 // sequence; within a sequence index 0 is the tile holding the last positions. Returns false for
@@ -94,13 +109,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     const int k_len = min(max(p.cu_seqlens_k[seq + 1] - k_start, 0), total_k - k_start);
     const int offset = k_len - q_len;  // bottom-right causal alignment
 
-    // Rows of this lane: column block cb -> tile row 64 wave + 32 cb + col.
+    // Rows of this lane: column block cb -> tile row 64 wave + 32 cb + col. S^T comes out of the
+    // MFMA exact (fp32 sums of bf16 products); scale * log2 e is applied in fp32 per score.
     int pos[2], head[2];
     bool valid[2];
     const float c2 = p.scale * kLog2e;
     bf16x8 q_op[2][4];
-    float m[2], dsum[2];
-    f32x16 acc[2][2];
+    float sink2[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const int r = wave * kRowsPerWave + cb * 32 + col;
@@ -113,20 +128,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             q_op[cb][ks] = valid[cb] ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * half) : zero_bf16x8();
-        // Sink fold: m starts at the head's sink, d at 1 (kept in the half-0 lane's partial sum).
-        m[cb] = p.sinks[head[cb]] * kLog2e;
-        dsum[cb] = (half == 0 && m[cb] != kNegInf) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int n = 0; n < 2; ++n) acc[cb][n] = zero_f32x16();
+        sink2[cb] = p.sinks[head[cb]] * kLog2e;
     }
 
     // Keys this tile's rows may see: [0, key_end).
     const int last_pos = min(first_pos + positions_per_tile, q_len) - 1;
     int key_end = p.causal ? min(k_len, last_pos + offset + 1) : k_len;
     key_end = key_end < 0 ? 0 : key_end;
-    // Tiles reaching past this key need masking (diagonal or sequence end).
+    // Keys below safe_end are visible to every row of the tile: KV tiles [0, mask_from) need no
+    // mask (the diagonal and the sequence end fall in the tiles after them).
     const int safe_end = p.causal ? min(k_len, first_pos + offset + 1) : k_len;
     const int num_tiles = (key_end + kKeyTile - 1) / kKeyTile;
+    const int mask_from = min(num_tiles, max(safe_end, 0) / kKeyTile);
 
     // K/V rows [0, key_end) of KV head g of this sequence; loads past the end return zeros.
     const __bf16* kbase = static_cast<const __bf16*>(p.k) + static_cast<int64_t>(k_start) * p.k_stride_tok +
@@ -163,113 +176,266 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     const int tr_row = 4 * half + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    if (num_tiles > 0) {
-        fetch(0);
-        stash(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < num_tiles; ++kt) {
+    float m[2], dsum[2];
+    f32x16 acc[2][2];
+
+    // S^T register r of block mb (32 keys) holds key key0 + 32 mb + 8 (r / 4) + 4 half + r % 4 of
+    // the lane's query row; P^T k-step u = 2 mb + r / 8 takes registers 8 (u % 2) .. + 7 of it.
+    auto v_step = [&](int buf, int u, bf16x8 (&vo)[2]) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const __bf16* vrow = &v_tile[buf][16 * u + tr_row][32 * n + tr_col];
+            const bf16x4 lo4 = lds_read_tr4(vrow);
+            const bf16x4 hi4 = lds_read_tr4(vrow + 8 * kVPitch);
+            vo[n] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto k_half = [&](int buf, int mb, bf16x8 (&ko)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            ko[ks] = *reinterpret_cast<const bf16x8*>(&k_tile[buf][32 * mb + col][16 * ks + 8 * half]);
+    };
+    // Exponentials exp2(c2 s - m) of registers [r0, r0 + nr) of one S^T block into P^T operands,
+    // with the row sum taken on the rounded values (v_dot2 with (1, 1)) so numerator and
+    // denominator use the same P. On the zero reference (m = 0) this is one multiply per score.
+    auto exp_regs = [&](const f32x16& sb, float neg_m, bool zero_ref, bf16x8 (&pp)[4], int mb, int r0, int nr,
+                        float& pa, float& pb) {
+#pragma unroll
+        for (int r = r0; r < r0 + nr; r += 2) {
+            bf16x2 pr;
+            pr[0] = (__bf16)exp2_fast(zero_ref ? sb[r] * c2 : fmaf(sb[r], c2, neg_m));
+            pr[1] = (__bf16)exp2_fast(zero_ref ? sb[r + 1] * c2 : fmaf(sb[r + 1], c2, neg_m));
+            pp[2 * mb + (r >> 3)][r & 7] = pr[0];
+            pp[2 * mb + (r >> 3)][(r & 7) + 1] = pr[1];
+            if (r & 2) pb = sum_bf16x2(pr, pb); else pa = sum_bf16x2(pr, pa);
+        }
+    };
+    // Causal / sequence-end mask of one S^T block: compare the compile-time key offset against
+    // one per-row relative limit.
+    auto mask_block = [&](f32x16& sb, int cb, int mb, int key0) {
+        const int limit = p.causal ? min(k_len, pos[cb] + offset + 1) : k_len;
+        const int rel = limit - key0 - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (32 * mb + 8 * (r >> 2) + (r & 3) >= rel) sb[r] = kNegInf;
+    };
+    auto wave_zero_ref = [&]() { return __all(m[0] == 0.0f && m[1] == 0.0f); };
+
+    // A plain tile (general reference, or zero reference with masking): all S^T first, then the
+    // softmax of each column block, then O^T += V^T . P^T.
+    auto plain_tile = [&](int kt, auto masked_tag, auto fast_tag, auto allow_switch_tag) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        constexpr bool kZero = decltype(fast_tag)::value;
+        constexpr bool kSwitch = decltype(allow_switch_tag)::value;
         const int buf = kt & 1;
         const int key0 = kt * kKeyTile;
         fetch(key0 + kKeyTile);  // next tile (zeros past the end), lands during this tile's math
         __builtin_amdgcn_sched_barrier(0);
-
-        // S^T blocks s[cb][mb]: keys key0 + 32 mb + 8 (r / 4) + 4 half + r % 4 (register r) of
-        // the lane's query row in column block cb.
-        bf16x8 k_op[2][4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                k_op[mb][ks] = *reinterpret_cast<const bf16x8*>(&k_tile[buf][32 * mb + col][16 * ks + 8 * half]);
-        const bool need_mask = key0 + kKeyTile > safe_end;
-
         f32x16 s[2][2];
-        bf16x8 p_op[2][4];
-        auto scores = [&](int cb) {
+        {
+            bf16x8 ko[2][4];
+            k_half(buf, 0, ko[0]);
+            k_half(buf, 1, ko[1]);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                s[cb][mb] = zero_f32x16();
+            for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) s[cb][mb] = mfma32x32x16(k_op[mb][ks], q_op[cb][ks], s[cb][mb]);
+                for (int mb = 0; mb < 2; ++mb) {
+                    s[cb][mb] = mfma32x32x16(ko[mb][0], q_op[cb][0], zero_f32x16());
+#pragma unroll
+                    for (int ks = 1; ks < 4; ++ks) s[cb][mb] = mfma32x32x16(ko[mb][ks], q_op[cb][ks], s[cb][mb]);
+                }
+        }
+        bf16x8 pp[2][4];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            if constexpr (kMasked) {
+                mask_block(s[cb][0], cb, 0, key0);
+                mask_block(s[cb][1], cb, 1, key0);
             }
-        };
-        // Online softmax of one column block; P goes to bf16 operands, row sums are taken on
-        // the rounded values (v_dot2 with (1, 1)) so numerator and denominator use the same P.
-        auto softmax = [&](int cb) {
-            if (need_mask) {
-                // Register r of block mb holds key key0 + 4 half + (32 mb + 8 (r / 4) + r % 4):
-                // compare the compile-time part against one per-row relative limit.
-                const int limit = p.causal ? min(k_len, pos[cb] + offset + 1) : k_len;
-                const int rel = limit - key0 - 4 * half;
+            float neg_m = 0.0f;
+            if constexpr (!kZero) {
+                // Running max with lazy rescaling.
+                float bmax = kNegInf;
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * mb + 8 * (r >> 2) + (r & 3) >= rel) s[cb][mb][r] = kNegInf;
-            }
-            float bmax = kNegInf;
+                    for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[cb][mb][r]);
+                bmax = max_xor32(bmax) * c2;  // scale > 0, so the max commutes with it
+                if (__any(bmax > m[cb] + kRescaleSlack)) {
+                    const float m_new = fmaxf(m[cb], bmax);
+                    const float alpha = exp2_fast(m[cb] - (m_new == kNegInf ? 0.0f : m_new));
+                    dsum[cb] *= alpha;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[cb][mb][r]);
-            bmax = max_xor32(bmax);
-            const float tmax = bmax * c2;
-            if (__any(tmax > m[cb] + kRescaleSlack)) {
-                const float m_new = fmaxf(m[cb], tmax);
-                const float alpha = exp2_fast(m[cb] - (m_new == kNegInf ? 0.0f : m_new));
-                dsum[cb] *= alpha;
-#pragma unroll
-                for (int n = 0; n < 2; ++n) acc[cb][n] *= alpha;
-                m[cb] = m_new;
-            }
-            const float neg_m = m[cb] == kNegInf ? 0.0f : -m[cb];
-            float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    bf16x2 pr;
-                    pr[0] = (__bf16)exp2_fast(fmaf(s[cb][mb][r], c2, neg_m));
-                    pr[1] = (__bf16)exp2_fast(fmaf(s[cb][mb][r + 1], c2, neg_m));
-                    // PV k-step u = 2 mb + r / 8 takes registers 8 (u % 2) .. + 7 of block mb.
-                    p_op[cb][2 * mb + (r >> 3)][r & 7] = pr[0];
-                    p_op[cb][2 * mb + (r >> 3)][(r & 7) + 1] = pr[1];
-                    ps[r & 3 ? 1 : 0] = sum_bf16x2(pr, ps[r & 3 ? 1 : 0]);
+                    for (int n = 0; n < 2; ++n) acc[cb][n] *= alpha;
+                    m[cb] = m_new;
                 }
-            dsum[cb] += ps[0] + ps[1];
-        };
-        // O^T += V^T . P^T over four 16-key steps; V^T operands by transpose reads.
-        bf16x8 v_op[4][2];
-        auto load_v = [&]() {
+                neg_m = m[cb] == kNegInf ? 0.0f : -m[cb];
+            }
+            float pa = 0.0f, pb = 0.0f;
+            exp_regs(s[cb][0], neg_m, kZero, pp[cb], 0, 0, 16, pa, pb);
+            exp_regs(s[cb][1], neg_m, kZero, pp[cb], 1, 0, 16, pa, pb);
+            dsum[cb] += pa + pb;
+        }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
+            bf16x8 vo[2];
+            v_step(buf, u, vo);
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const __bf16* vrow = &v_tile[buf][16 * u + tr_row][32 * n + tr_col];
-                    const bf16x4 lo4 = lds_read_tr4(vrow);
-                    const bf16x4 hi4 = lds_read_tr4(vrow + 8 * kVPitch);
-                    v_op[u][n] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) acc[cb][n] = mfma32x32x16(vo[n], pp[cb][u], acc[cb][n]);
+        }
+        if constexpr (kSwitch) {
+            // Rows whose running max is moderate move to the zero reference (exact up to one
+            // rounding of O and d), after this tile's P has been accumulated relative to the old
+            // reference.
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                if (m[cb] != 0.0f && m[cb] >= -kZeroRefLimit && m[cb] <= kZeroRefLimit) {
+                    const float alpha = exp2_fast(m[cb]);
+                    dsum[cb] *= alpha;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) acc[cb][n] *= alpha;
+                    m[cb] = 0.0f;
                 }
-        };
-        auto pv = [&](int cb) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) acc[cb][n] = mfma32x32x16(v_op[u][n], p_op[cb][u], acc[cb][n]);
-        };
-
-        scores(0);
-        scores(1);
-        softmax(0);
-        softmax(1);
-        load_v();
-        pv(0);
-        pv(1);
-
+            }
+        }
         stash(buf ^ 1);  // the other buffer was released by the previous barrier
         __syncthreads();
+    };
+
+    // An unmasked tile with every row of the wave on the zero reference. The MFMA chains and the
+    // exponentials are interleaved by hand: each group of four MFMAs carries the exponentials whose
+    // inputs are ready, so the matrix and vector pipes of the wave work at the same time.
+    //   slot 1: S00           slot 2: S10 | E00       slot 3: S01 | E10
+    //   slot 4: PV(u0) | E01a slot 5: S11 | E01b      slot 6: PV(u1) | E11a
+    //   slot 7: PV(u2) | E11b slot 8: PV(u3)
+    // (S_cb,mb: scores of column block cb, key half mb; E: its exponentials; PV(u): k-step u of
+    // O^T += V^T . P^T for both column blocks.)
+    auto fast_tile = [&](int kt) {
+        const int buf = kt & 1;
+        const int key0 = kt * kKeyTile;
+        fetch(key0 + kKeyTile);
+        __builtin_amdgcn_sched_barrier(0);
+        float ps0a = 0.0f, ps0b = 0.0f, ps1a = 0.0f, ps1b = 0.0f;
+        f32x16 s00, s10, s01, s11;
+        bf16x8 pp0[4], pp1[4];
+        bf16x8 k0[4], k1[4];
+        k_half(buf, 0, k0);
+        s00 = mfma32x32x16(k0[0], q_op[0][0], zero_f32x16());
+#pragma unroll
+        for (int ks = 1; ks < 4; ++ks) s00 = mfma32x32x16(k0[ks], q_op[0][ks], s00);
+        k_half(buf, 1, k1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s10 = j == 0 ? mfma32x32x16(k0[0], q_op[1][0], zero_f32x16()) : mfma32x32x16(k0[j], q_op[1][j], s10);
+            exp_regs(s00, 0.0f, true, pp0, 0, 4 * j, 4, ps0a, ps0b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s01 = j == 0 ? mfma32x32x16(k1[0], q_op[0][0], zero_f32x16()) : mfma32x32x16(k1[j], q_op[0][j], s01);
+            exp_regs(s10, 0.0f, true, pp1, 0, 4 * j, 4, ps1a, ps1b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 va[2], vb[2];
+        v_step(buf, 0, va);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j >> 1][j & 1] = mfma32x32x16(va[j & 1], (j >> 1) ? pp1[0] : pp0[0], acc[j >> 1][j & 1]);
+            exp_regs(s01, 0.0f, true, pp0, 1, 2 * j, 2, ps0a, ps0b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        v_step(buf, 1, vb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s11 = j == 0 ? mfma32x32x16(k1[0], q_op[1][0], zero_f32x16()) : mfma32x32x16(k1[j], q_op[1][j], s11);
+            exp_regs(s01, 0.0f, true, pp0, 1, 8 + 2 * j, 2, ps0a, ps0b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        v_step(buf, 2, va);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j >> 1][j & 1] = mfma32x32x16(vb[j & 1], (j >> 1) ? pp1[1] : pp0[1], acc[j >> 1][j & 1]);
+            exp_regs(s11, 0.0f, true, pp1, 1, 2 * j, 2, ps1a, ps1b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        v_step(buf, 3, vb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j >> 1][j & 1] = mfma32x32x16(va[j & 1], (j >> 1) ? pp1[2] : pp0[2], acc[j >> 1][j & 1]);
+            exp_regs(s11, 0.0f, true, pp1, 1, 8 + 2 * j, 2, ps1a, ps1b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[j >> 1][j & 1] = mfma32x32x16(vb[j & 1], (j >> 1) ? pp1[3] : pp0[3], acc[j >> 1][j & 1]);
+        dsum[0] += ps0a + ps0b;
+        dsum[1] += ps1a + ps1b;
+        stash(buf ^ 1);
+        __syncthreads();
+    };
+
+    using False = std::integral_constant<bool, false>;
+    using True = std::integral_constant<bool, true>;
+    // All KV tiles of the work-group. With kAllowFast, rows move to the zero reference as soon as
+    // their running max allows it, and a wave whose rows all have moved runs fast tiles.
+    auto process = [&](auto allow_fast_tag) {
+        constexpr bool kAllowFast = decltype(allow_fast_tag)::value;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            // Sink fold: m starts at the head's sink, d at 1 (kept in the half-0 lane's share).
+            m[cb] = sink2[cb];
+            dsum[cb] = (half == 0 && m[cb] != kNegInf) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) acc[cb][n] = zero_f32x16();
+        }
+        if (num_tiles > 0) {
+            fetch(0);
+            stash(0);
+        }
+        __syncthreads();
+        int kt = 0;
+        for (; kt < mask_from; ++kt) {
+            if (kAllowFast && wave_zero_ref()) break;
+            plain_tile(kt, False(), False(), allow_fast_tag);
+        }
+        if constexpr (kAllowFast) {
+            for (; kt < mask_from; ++kt) fast_tile(kt);
+        }
+        for (; kt < num_tiles; ++kt) {
+            if (kAllowFast && wave_zero_ref())
+                plain_tile(kt, True(), True(), False());
+            else
+                plain_tile(kt, True(), False(), allow_fast_tag);
+        }
+    };
+
+    // Zero-reference tiles leave p = exp2(s) unbounded above. If any row's d left the range where
+    // that is safe (d > 2^64, or any non-finite d or O), the whole work-group starts again with
+    // the running-max reference only; the decision is work-group wide because the waves share
+    // the K/V tiles and their barriers.
+    __shared__ int redo_general;
+    process(True());
+    bool bad = false;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        bad |= !(dsum[cb] <= kFastSumLimit);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bad |= !__builtin_isfinite(acc[cb][n][r]);
     }
+    if (tid == 0) redo_general = 0;
+    __syncthreads();
+    if (__any(bad) && lane == 0) redo_general = 1;
+    __syncthreads();
+    if (redo_general) process(False());
 
     // Epilogue: out = acc / d. Lane holds d-channels 32n + 8 (r / 4) + 4 half + r % 4.
 #pragma unroll

@@ -170,6 +170,22 @@ def test_prefill_bf16_small(name, lq, lk, hq, hkv, causal, sr):
     check_bf16(out32, ref, f"prefill {name} f32-out")
 
 
+@pytest.mark.parametrize("factor,causal", [(8.0, True), (32.0, True), (32.0, False)],
+                         ids=["x8_causal", "x32_causal", "x32_noncausal"])
+def test_prefill_bf16_logits_grow_after_early_keys(factor, causal):
+    """Keys past the first 256 scaled by a power of two (exact in bf16): rows settle on small
+    logits first, then meet logits up to ~factor times larger. x8 keeps exp2 of the logits in
+    fp32 range; x32 does not, which the kernel must detect and recompute."""
+    sa = _sa()
+    case = workloads.make_prefill([600, 300], num_q_heads=64, num_kv_heads=8, seed=int(factor) + causal,
+                                  causal=causal)
+    for start, length in ((0, 600), (600, 300)):
+        case.k[start + 256:start + length] *= factor
+    out = run_prefill(sa, case)
+    ref, _ = oracle_prefill(case)
+    check_bf16(out, ref, f"prefill keys x{factor}")
+
+
 def test_prefill_bf16_sink_neg_inf_is_plain_attention():
     sa = _sa()
     case = workloads.make_prefill([130, 64], num_q_heads=64, num_kv_heads=8, seed=7)

@@ -17,6 +17,7 @@ The same JSON line also carries:
 * ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
+                      [--no-hot]
 """
 from __future__ import annotations
 
@@ -138,8 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--hot", action="store_true",
-                    help="also time steps that reuse one K/V set (cache-resident; not the headline)")
+    ap.add_argument("--no-hot", action="store_true",
+                    help="skip the steps that reuse one K/V set (cache-resident; never the headline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the hot path here is a "
@@ -161,6 +162,15 @@ def main():
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
+    # The same copy, timed: a measured HBM ceiling (read + write) beside the spec peak.
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        calib_dst.copy_(calib_src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * CALIB_BYTES / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
     del calib_src, calib_dst
 
     # ---------------------------------------------------------------- decode workload (value)
@@ -230,7 +240,7 @@ def main():
     ms_split = _time_graph(_capture(split, n_rep, torch), n_rep, torch)
     ms_merge = _time_graph(_capture(merge, n_rep, torch), n_rep, torch)
     ms_two = _time_graph(_capture(split_merge, n_rep, torch), n_rep, torch)
-    ms_hot = _time_graph(_capture(step_hot, n_rep, torch), n_rep, torch) if args.hot else None
+    ms_hot = _time_graph(_capture(step_hot, n_rep, torch), n_rep, torch) if not args.no_hot else None
     ms_eager = None
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -278,6 +288,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": split_bytes,
             "avg_launch_us": round(ms_split * 1e3, 3),
+            "measured_copy_gbs": round(copy_gbs, 1),
+            "frac_of_measured_copy": round(split_gbs / copy_gbs, 4),
         },
         "decode_detail": {
             "split_us": round(ms_split * 1e3, 3), "merge_us": round(ms_merge * 1e3, 3),

@@ -321,60 +321,87 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         f32x16 s00, s10, s01, s11;
         bf16x8 pp0[4], pp1[4];
         bf16x8 k0[4], k1[4];
+        // A slot ends with an empty asm that takes and returns every value the slot produces:
+        // the code generator may otherwise move the (side-effect free) exponentials across slot
+        // boundaries; inside a slot, group barriers ask for one MFMA per n VALU instructions.
+#define SA_PIN_ACC() asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]))
+#define SA_INTERLEAVE(n_mfma, n_valu)                                    \
+    do {                                                                 \
+        for (int i_ = 0; i_ < (n_mfma); ++i_) {                          \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+            __builtin_amdgcn_sched_group_barrier(0x002, (n_valu), 0);    \
+        }                                                                \
+    } while (0)
+        // slot 1: S00
         k_half(buf, 0, k0);
         s00 = mfma32x32x16(k0[0], q_op[0][0], zero_f32x16());
 #pragma unroll
         for (int ks = 1; ks < 4; ++ks) s00 = mfma32x32x16(k0[ks], q_op[0][ks], s00);
         k_half(buf, 1, k1);
+        asm volatile("" : "+v"(s00));
         __builtin_amdgcn_sched_barrier(0);
+        // slot 2: S10 | E00
+        s10 = mfma32x32x16(k0[0], q_op[1][0], zero_f32x16());
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            s10 = j == 0 ? mfma32x32x16(k0[0], q_op[1][0], zero_f32x16()) : mfma32x32x16(k0[j], q_op[1][j], s10);
-            exp_regs(s00, 0.0f, true, pp0, 0, 4 * j, 4, ps0a, ps0b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int ks = 1; ks < 4; ++ks) s10 = mfma32x32x16(k0[ks], q_op[1][ks], s10);
+        exp_regs(s00, 0.0f, true, pp0, 0, 0, 16, ps0a, ps0b);
+        SA_INTERLEAVE(4, 12);
+        asm volatile("" : "+v"(s10), "+v"(pp0[0]), "+v"(pp0[1]), "+v"(ps0a), "+v"(ps0b));
+        __builtin_amdgcn_sched_barrier(0);
+        // slot 3: S01 | E10
+        s01 = mfma32x32x16(k1[0], q_op[0][0], zero_f32x16());
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            s01 = j == 0 ? mfma32x32x16(k1[0], q_op[0][0], zero_f32x16()) : mfma32x32x16(k1[j], q_op[0][j], s01);
-            exp_regs(s10, 0.0f, true, pp1, 0, 4 * j, 4, ps1a, ps1b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int ks = 1; ks < 4; ++ks) s01 = mfma32x32x16(k1[ks], q_op[0][ks], s01);
+        exp_regs(s10, 0.0f, true, pp1, 0, 0, 16, ps1a, ps1b);
         bf16x8 va[2], vb[2];
         v_step(buf, 0, va);
+        SA_INTERLEAVE(4, 12);
+        asm volatile("" : "+v"(s01), "+v"(pp1[0]), "+v"(pp1[1]), "+v"(ps1a), "+v"(ps1b));
         __builtin_amdgcn_sched_barrier(0);
+        // slot 4: PV(u0) | E01 first half
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             acc[j >> 1][j & 1] = mfma32x32x16(va[j & 1], (j >> 1) ? pp1[0] : pp0[0], acc[j >> 1][j & 1]);
-            exp_regs(s01, 0.0f, true, pp0, 1, 2 * j, 2, ps0a, ps0b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        exp_regs(s01, 0.0f, true, pp0, 1, 0, 8, ps0a, ps0b);
         v_step(buf, 1, vb);
+        SA_INTERLEAVE(4, 6);
+        SA_PIN_ACC();
+        asm volatile("" : "+v"(pp0[2]), "+v"(ps0a), "+v"(ps0b));
         __builtin_amdgcn_sched_barrier(0);
+        // slot 5: S11 | E01 second half
+        s11 = mfma32x32x16(k1[0], q_op[1][0], zero_f32x16());
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            s11 = j == 0 ? mfma32x32x16(k1[0], q_op[1][0], zero_f32x16()) : mfma32x32x16(k1[j], q_op[1][j], s11);
-            exp_regs(s01, 0.0f, true, pp0, 1, 8 + 2 * j, 2, ps0a, ps0b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        v_step(buf, 2, va);
+        for (int ks = 1; ks < 4; ++ks) s11 = mfma32x32x16(k1[ks], q_op[1][ks], s11);
+        exp_regs(s01, 0.0f, true, pp0, 1, 8, 8, ps0a, ps0b);
+        SA_INTERLEAVE(4, 6);
+        asm volatile("" : "+v"(s11), "+v"(pp0[3]), "+v"(ps0a), "+v"(ps0b));
         __builtin_amdgcn_sched_barrier(0);
+        // slot 6: PV(u1) | E11 first half
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             acc[j >> 1][j & 1] = mfma32x32x16(vb[j & 1], (j >> 1) ? pp1[1] : pp0[1], acc[j >> 1][j & 1]);
-            exp_regs(s11, 0.0f, true, pp1, 1, 2 * j, 2, ps1a, ps1b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        v_step(buf, 3, vb);
+        exp_regs(s11, 0.0f, true, pp1, 1, 0, 8, ps1a, ps1b);
+        v_step(buf, 2, va);
+        SA_INTERLEAVE(4, 6);
+        SA_PIN_ACC();
+        asm volatile("" : "+v"(pp1[2]), "+v"(ps1a), "+v"(ps1b));
         __builtin_amdgcn_sched_barrier(0);
+        // slot 7: PV(u2) | E11 second half
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             acc[j >> 1][j & 1] = mfma32x32x16(va[j & 1], (j >> 1) ? pp1[2] : pp0[2], acc[j >> 1][j & 1]);
-            exp_regs(s11, 0.0f, true, pp1, 1, 8 + 2 * j, 2, ps1a, ps1b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        exp_regs(s11, 0.0f, true, pp1, 1, 8, 8, ps1a, ps1b);
+        v_step(buf, 3, vb);
+        SA_INTERLEAVE(4, 6);
+        SA_PIN_ACC();
+        asm volatile("" : "+v"(pp1[3]), "+v"(ps1a), "+v"(ps1b));
+        __builtin_amdgcn_sched_barrier(0);
+        // slot 8: PV(u3)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[j >> 1][j & 1] = mfma32x32x16(vb[j & 1], (j >> 1) ? pp1[3] : pp0[3], acc[j >> 1][j & 1]);
+#undef SA_PIN_ACC
+#undef SA_INTERLEAVE
         dsum[0] += ps0a + ps0b;
         dsum[1] += ps1a + ps1b;
         stash(buf ^ 1);

@@ -254,10 +254,22 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
             }
         }
         const int64_t row = (static_cast<int64_t>(b) * p.num_q_heads + g * group + hc) * p.num_chunks + chunk;
-        p.partial_o[row * kHeadDim + d] = wsum > 0.0f ? osum / wsum : 0.0f;
-        if (d == 0) {
-            p.partial_m[row] = wsum > 0.0f ? big * kLn2 : kNegInf;
-            p.partial_d[row] = wsum;
+        const float o = wsum > 0.0f ? osum / wsum : 0.0f;
+        const float m_nat = wsum > 0.0f ? big * kLn2 : kNegInf;
+        if constexpr (kFused) {
+            // Write-through stores: the release fence below then has no dirty L2 lines to write
+            // back, which is most of its cost (38 -> 34 us on 8 x 8192 keys).
+            __hip_atomic_store(&p.partial_o[row * kHeadDim + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (d == 0) {
+                __hip_atomic_store(&p.partial_m[row], m_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(&p.partial_d[row], wsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        } else {
+            p.partial_o[row * kHeadDim + d] = o;
+            if (d == 0) {
+                p.partial_m[row] = m_nat;
+                p.partial_d[row] = wsum;
+            }
         }
     }
 

@@ -16,5 +16,7 @@ from .sink_attention import (  # noqa: F401
     online_row,
     prefill,
     prefill_at,
+    prefill_split,
     sink_softmax,
+    split_size,
 )

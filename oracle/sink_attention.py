@@ -32,7 +32,8 @@ Readings taken where the page is silent or garbled (each one is also listed in t
 * Split-KV state per chunk is (m, d, o): m the chunk's max logit (with the sink when the chunk is
   the first), d = sum of e^(z - m) over the chunk's terms, o = the chunk's softmax-weighted mean of
   V.  An empty chunk that is not the first is (-inf, 0, 0).  Merging weighs chunk c by
-  d_c * e^(m_c - M), M the largest m_c (the log-sum-exp merge).
+  d_c * e^(m_c - M), M the largest m_c (the log-sum-exp merge).  Prefill split along the KV length
+  follows the same first-chunk rule: only split 0 of a sequence carries the sink.
 
 Every function here is pinned by tests that do not call back into it for their expected values:
 closed forms, a 50-digit brute force, the float64 PyTorch SDPA library routine, identities, and
@@ -224,6 +225,62 @@ def decode_split(q, k, v, sinks, seqlens_k, num_chunks, scale):
                 z = scale * (keys @ q[b, h])
                 m, d, o = chunk_state(z, vals, sinks[h] if c == 0 else None)
                 po[b, h, c], pm[b, h, c], pd[b, h, c] = o, m, d
+    return po, pm, pd
+
+
+def split_size(num_keys: int, num_splits: int, align: int = 64) -> int:
+    """Keys per KV split of one prefill sequence: ceil(Lk / S) rounded up to a multiple of ``align``.
+
+    A convention of the split-KV prefill call (its splits start on whole key tiles), not of the
+    method: any split with the sink in split 0 merges to the same result.
+    """
+    per = -(-int(num_keys) // int(num_splits))
+    return -(-per // align) * align
+
+
+def prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, num_splits, align=64):
+    """Split-KV prefill partials: split ``j`` of sequence b covers its keys
+    ``[j*ks_b, min((j+1)*ks_b, Lk_b))`` with ``ks_b = split_size(Lk_b, S)``; a query row's state in
+    a split is taken over the split's keys that the row may see (causal reading as in ``prefill``),
+    with the sink in split 0 only (the first-chunk rule, applied to prefill).
+
+    Each state is computed from its definition: the split's scaled logits, the sink column appended
+    when j = 0, m = their max, d = sum of e^(term - m), o = the e^(z - m)-weighted mean of V. A split
+    with no finite term is (-inf, 0, 0).
+    Returns ``(partial_o [Tq, Hq, S, D], partial_m [Tq, Hq, S], partial_d [Tq, Hq, S])``.
+    """
+    q, k, v, sinks = _f64(q), _f64(k), _f64(v), _f64(sinks)
+    cu_q = np.asarray(cu_seqlens_q, dtype=np.int64)
+    cu_k = np.asarray(cu_seqlens_k, dtype=np.int64)
+    t_q, h_q, dim = q.shape
+    group = _group(h_q, k.shape[1])
+    po = np.zeros((t_q, h_q, num_splits, dim))
+    pm = np.full((t_q, h_q, num_splits), NEG_INF)
+    pd = np.zeros((t_q, h_q, num_splits))
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        n_q, n_k = q1 - q0, k1 - k0
+        if n_q == 0:
+            continue
+        ks = split_size(n_k, num_splits, align) if n_k > 0 else 1
+        rows = np.arange(n_q)
+        allowed = causal_allowed(rows, n_q, n_k) if causal else np.ones((n_q, n_k), dtype=bool)
+        for h in range(h_q):
+            g = h // group
+            z = scale * (q[q0:q1, h] @ k[k0:k1, g].T)  # [n_q, n_k]
+            z = np.where(allowed, z, NEG_INF)
+            for j in range(num_splits):
+                lo, hi = min(j * ks, n_k), min((j + 1) * ks, n_k)
+                zj = z[:, lo:hi]
+                terms = zj if j > 0 else np.concatenate([zj, np.full((n_q, 1), sinks[h])], axis=1)
+                m = terms.max(axis=1, initial=NEG_INF)
+                live = ~np.isneginf(m)
+                shift = np.where(live, m, 0.0)
+                e = np.exp(zj - shift[:, None])  # e^(-inf) = 0 for keys the row may not see
+                d = e.sum(axis=1) + (np.exp(sinks[h] - shift) if j == 0 else 0.0)
+                d = np.where(live, d, 0.0)
+                o = np.where(live[:, None], (e @ v[k0 + lo:k0 + hi, g]) / np.where(live, d, 1.0)[:, None], 0.0)
+                po[q0:q1, h, j], pm[q0:q1, h, j], pd[q0:q1, h, j] = o, m, d
     return po, pm, pd
 
 

@@ -315,6 +315,69 @@ def test_p9_sink_is_not_scaled():
 
 
 # ----------------------------------------------------------------------------- P10: key order
+@pytest.mark.parametrize("causal", [True, False])
+def test_p4_prefill_split_merge_equals_unsplit(causal):
+    """Split-KV prefill (sink in split 0 only), merged, equals the unsplit prefill for every split
+    count, with varlen sequences, an empty sequence, Lq < Lk (append) and splits past the end."""
+    lens_q, lens_k = [9, 0, 5, 12], [9, 0, 70, 12]
+    cu_q, cu_k = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    q = _rand((cu_q[-1], 4, D), 91)
+    k = _rand((cu_k[-1], 2, D), 92)
+    v = _rand((cu_k[-1], 2, D), 93)
+    sinks = _rand(4, 94) * 2
+    ref, ref_lse = oracle.prefill(q, k, v, sinks, cu_q, cu_k, 0.125, causal)
+    for splits in range(1, 7):
+        for align in (1, 4, 64):
+            po, pm, pd = oracle.prefill_split(q, k, v, sinks, cu_q, cu_k, 0.125, causal, splits, align)
+            out, lse = oracle.merge(po, pm, pd)
+            np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_split_states_follow_the_chunk_definition_and_boundaries():
+    """Each split's state is the chunk state of the row's visible keys inside the split's
+    boundaries [j*ks, (j+1)*ks), ks = ceil(Lk / S) rounded up to the alignment."""
+    n_q, n_k, splits, align = 6, 23, 3, 4
+    q = _rand((n_q, 1, D), 95)
+    k = _rand((n_k, 1, D), 96)
+    v = _rand((n_k, 1, D), 97)
+    sink = 0.3
+    assert oracle.split_size(23, 3, 4) == 8 and oracle.split_size(23, 3, 64) == 64
+    assert oracle.split_size(128, 2, 64) == 64 and oracle.split_size(129, 2, 64) == 128
+    po, pm, pd = oracle.prefill_split(q, k, v, [sink], [0, n_q], [0, n_k], 0.5, True, splits, align)
+    for i in range(n_q):
+        last = i + n_k - n_q  # bottom-right causal: keys 0..last are visible
+        for j in range(splits):
+            lo, hi = 8 * j, min(8 * j + 8, last + 1)
+            z = 0.5 * np.array([float(q[i, 0] @ k[t, 0]) for t in range(lo, max(lo, hi))])
+            m, d, o = oracle.chunk_state(z, v[lo:max(lo, hi), 0], sink if j == 0 else None)
+            assert pm[i, 0, j] == pytest.approx(m, abs=0) if math.isinf(m) else pm[i, 0, j] == pytest.approx(m, rel=1e-13)
+            assert pd[i, 0, j] == pytest.approx(d, rel=1e-13, abs=0)
+            np.testing.assert_allclose(po[i, 0, j], o, rtol=1e-12, atol=1e-14)
+
+
+def test_prefill_split_mutation_sink_in_every_split_is_caught():
+    """The first-chunk rule matters for prefill too: a sink folded into every split breaks the
+    merge identity."""
+    n = 40
+    q = _rand((n, 1, D), 98)
+    k = _rand((n, 1, D), 99)
+    v = _rand((n, 1, D), 100)
+    sink = 1.5
+    ref, _ = oracle.prefill(q, k, v, [sink], [0, n], [0, n], 0.125, True)
+    po, pm, pd = oracle.prefill_split(q, k, v, [sink], [0, n], [0, n], 0.125, True, 4, 4)
+    # Plant the sink in splits 1..3 of every row by refolding its term into (m, d, o).
+    for j in range(1, 4):
+        m_old, d_old, o_old = pm[:, 0, j], pd[:, 0, j], po[:, 0, j]
+        m_new = np.maximum(m_old, sink)
+        d_new = np.where(np.isneginf(m_old), 0.0, d_old * np.exp(m_old - m_new)) + np.exp(sink - m_new)
+        w_old = np.where(np.isneginf(m_old), 0.0, d_old * np.exp(m_old - m_new))
+        po[:, 0, j] = (w_old[:, None] * o_old) / d_new[:, None]
+        pm[:, 0, j], pd[:, 0, j] = m_new, d_new
+    bad, _ = oracle.merge(po, pm, pd)
+    assert np.max(np.abs(bad - ref)) > 1e-3
+
+
 def test_p10_noncausal_output_is_invariant_under_key_permutation():
     n = 29
     q = _rand((11, 4, D), 71)

@@ -14,6 +14,8 @@ The same JSON line also carries:
   WRITE_SIZE summary when it was taken on the current kernel source, else null;
 * ``prefill``: causal prefill of one 8192-token sequence (64/8 heads, bf16), TFLOP/s over the
   allowed causal pairs (4 * D per pair) against the 2.5 PFLOP/s dense bf16 MFMA peak;
+* ``prefill_append``: 512 new tokens against a 32768-key cache, unsplit and split 4 ways along the
+  KV length (sinkattn_prefill_split + sinkattn_decode_merge);
 * ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
@@ -333,6 +335,44 @@ def main():
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                          "algorithmic_flop_per_launch": flops},
+        }
+
+    # ---------------------------------------------------------------- split-KV (append) prefill
+    if not args.no_prefill:
+        # Chunked prefill: 512 new tokens against a 32768-key cache. Its 16 query tiles x 8 KV heads
+        # are 128 work-groups, half a GPU; splitting the KV length 4 ways gives 512 (merged after).
+        _log("generating append workload (512 new tokens x 32768 keys, 64/8 heads, bf16)")
+        app = workloads.make_prefill([512], [32768], seed=1006)
+        a_pairs = workloads.prefill_causal_pairs(app)
+        a_flops = 4.0 * dim * app.q.shape[1] * a_pairs
+        aq, ak, av = app.q.to(dev), app.k.to(dev), app.v.to(dev)
+        as_, acq, ack = app.sinks.to(dev), app.cu_seqlens_q.to(dev), app.cu_seqlens_k.to(dev)
+        aout = torch.empty_like(aq)
+        splits = 4  # measured best on this shape: 2 -> 322 us, 4 -> 285 us, 8 -> 289 us, 16 -> 304 us
+        apo = torch.empty((aq.shape[0], aq.shape[1], splits, dim), dtype=torch.float32, device=dev)
+        apm = torch.empty((aq.shape[0], aq.shape[1], splits), dtype=torch.float32, device=dev)
+        apd = torch.empty_like(apm)
+
+        def app_plain(i):
+            sa.prefill(aq, ak, av, as_, acq, ack, app.scale, True, out=aout)
+
+        def app_split(i):
+            sa.prefill_split(aq, ak, av, as_, acq, ack, app.scale, True, splits, apo, apm, apd)
+            sa.decode_merge(apo, apm, apd, out=aout)
+
+        n_app = max(5, args.steps // 2)
+        ms_plain = _time_graph(_capture(app_plain, n_app, torch), n_app, torch, replays=2)
+        ms_split = _time_graph(_capture(app_split, n_app, torch), n_app, torch, replays=2)
+        _log(f"append prefill: unsplit {ms_plain * 1e3:.1f} us, {splits}-way KV split + merge "
+             f"{ms_split * 1e3:.1f} us")
+        result["prefill_append"] = {
+            "workload": "prefill_append_q512_k32768_hq64_hkv8_d64_causal",
+            "kv_splits": splits,
+            "unsplit_us": round(ms_plain * 1e3, 2),
+            "split_plus_merge_us": round(ms_split * 1e3, 2),
+            "unsplit_tflops": round(a_flops / (ms_plain * 1e-3) / 1e12, 2),
+            "split_tflops": round(a_flops / (ms_split * 1e-3) / 1e12, 2),
+            "algorithmic_flop": a_flops,
         }
 
     # ---------------------------------------------------------------- CPU oracle baseline

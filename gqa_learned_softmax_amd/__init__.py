@@ -14,8 +14,8 @@ import torch
 from . import _lib
 from ._lib import SinkAttnError  # noqa: F401
 
-__all__ = ["prefill", "decode_split", "decode_merge", "decode", "decode_fused", "decode_workspace",
-           "SinkAttnError", "version"]
+__all__ = ["prefill", "prefill_split", "prefill_kv_split", "decode_split", "decode_merge", "decode",
+           "decode_fused", "decode_workspace", "SinkAttnError", "version"]
 
 
 def version() -> int:
@@ -33,6 +33,32 @@ def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal=True, out=
         _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
         _lib.ref(d[5]), float(scale), 1 if causal else 0, _lib.ref(d[6]), _lib.stream_handle(dev)))
     return out
+
+
+def prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, num_splits,
+                  partial_o=None, partial_m=None, partial_d=None):
+    """``sinkattn_prefill_split``: returns (partial_o [Tq,Hq,S,D], partial_m [Tq,Hq,S], partial_d)."""
+    tq, hq, dim = q.shape
+    if partial_o is None:
+        partial_o = torch.empty((tq, hq, num_splits, dim), dtype=torch.float32, device=q.device)
+    if partial_m is None:
+        partial_m = torch.empty((tq, hq, num_splits), dtype=torch.float32, device=q.device)
+    if partial_d is None:
+        partial_d = torch.empty((tq, hq, num_splits), dtype=torch.float32, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, partial_o, partial_m, partial_d)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, partial_o, partial_m, partial_d)]
+    _lib.check(_lib.lib.sinkattn_prefill_split(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]), _lib.ref(d[5]),
+        float(scale), 1 if causal else 0, int(num_splits), _lib.ref(d[6]), _lib.ref(d[7]), _lib.ref(d[8]),
+        _lib.stream_handle(dev)))
+    return partial_o, partial_m, partial_d
+
+
+def prefill_kv_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, num_splits, out=None,
+                     return_lse=False):
+    """Split-KV prefill then the log-sum-exp merge (partials allocated with torch); out [Tq, Hq, D]."""
+    po, pm, pd = prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, num_splits)
+    return decode_merge(po, pm, pd, out=out, out_dtype=q.dtype, return_lse=return_lse)
 
 
 def decode_split(q, k, v, sinks, seqlens_k, num_chunks, scale, partial_o=None, partial_m=None,

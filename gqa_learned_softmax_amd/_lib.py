@@ -56,6 +56,8 @@ _P = ctypes.POINTER(Tensor)
 EXPORTS = {
     "sinkattn_prefill": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int, _P, ctypes.c_void_p],
                          ctypes.c_int),
+    "sinkattn_prefill_split": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int, ctypes.c_int, _P, _P, _P,
+                                ctypes.c_void_p], ctypes.c_int),
     "sinkattn_decode_split": ([_P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P,
                                ctypes.c_void_p], ctypes.c_int),
     "sinkattn_decode_merge": ([_P, _P, _P, ctypes.c_int, _P, _P, ctypes.c_void_p], ctypes.c_int),

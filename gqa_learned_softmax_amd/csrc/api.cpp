@@ -276,39 +276,27 @@ WorkspaceLayout workspace_layout(int64_t batch, int64_t hq, int64_t hkv, int64_t
     return w;
 }
 
-}  // namespace
-
-extern "C" {
-
-sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
-                                 const sinkattn_tensor* v, const sinkattn_tensor* sinks,
-                                 const sinkattn_tensor* cu_seqlens_q,
-                                 const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
-                                 const sinkattn_tensor* out, void* stream) {
-    g_last_error.clear();
+// Validation shared by the prefill calls (everything but the outputs); fills p.
+sinkattn_status check_prefill_inputs(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                     const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                     const sinkattn_tensor* cu_seqlens_q,
+                                     const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
+                                     sinkattn::PrefillParams& p) {
     SA_TRY(check_desc(q, "q", 3));
     SA_TRY(check_desc(k, "k", 3));
     SA_TRY(check_desc(v, "v", 3));
-    SA_TRY(check_desc(out, "out", 3));
     SA_TRY(check_desc(cu_seqlens_q, "cu_seqlens_q", 1));
     SA_TRY(check_desc(cu_seqlens_k, "cu_seqlens_k", 1));
-
     if (q->dtype != SINKATTN_BF16 && q->dtype != SINKATTN_F32)
         return fail(SINKATTN_ERR_DTYPE, "q: dtype must be bf16 or f32");
     SA_TRY(check_dtype(k, "k", q->dtype));
     SA_TRY(check_dtype(v, "v", q->dtype));
-    if (q->dtype == SINKATTN_F32) SA_TRY(check_dtype(out, "out", SINKATTN_F32));
-    else if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
-        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
 
     const int64_t tq = q->shape[0], hq = q->shape[1], dim = q->shape[2];
     const int64_t tk = k->shape[0], hkv = k->shape[1];
     for (int i = 0; i < 3; ++i)
         if (v->shape[i] != k->shape[i])
             return fail(SINKATTN_ERR_SHAPE, "v: shape differs from k");
-    for (int i = 0; i < 3; ++i)
-        if (out->shape[i] != q->shape[i])
-            return fail(SINKATTN_ERR_SHAPE, "out: shape differs from q");
     if (k->shape[2] != dim) return fail(SINKATTN_ERR_SHAPE, "k: head_dim differs from q");
     if (hkv <= 0 || hq <= 0 || hq % hkv != 0)
         return fail(SINKATTN_ERR_SHAPE, "query heads (%lld) must be a positive multiple of KV heads (%lld)",
@@ -333,14 +321,56 @@ sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor
     if ((tk + 128) * k->stride[0] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
         (tk + 128) * v->stride[0] * elem_size(v->dtype) >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "K/V exceed 2 GiB of addressable rows");
-
     SA_TRY(check_data(q, "q"));
     SA_TRY(check_data(k, "k"));
     SA_TRY(check_data(v, "v"));
-    SA_TRY(check_data(out, "out"));
     SA_TRY(check_rows(q, "q"));
     SA_TRY(check_rows(k, "k"));
     SA_TRY(check_rows(v, "v"));
+
+    p.q = q->data;
+    p.k = k->data;
+    p.v = v->data;
+    p.sinks = static_cast<const float*>(sinks->data);
+    p.cu_seqlens_q = static_cast<const int32_t*>(cu_seqlens_q->data);
+    p.cu_seqlens_k = static_cast<const int32_t*>(cu_seqlens_k->data);
+    p.q_stride_tok = q->stride[0];
+    p.q_stride_head = q->stride[1];
+    p.k_stride_tok = k->stride[0];
+    p.k_stride_head = k->stride[1];
+    p.v_stride_tok = v->stride[0];
+    p.v_stride_head = v->stride[1];
+    p.total_q = tq;
+    p.total_k = tk;
+    p.num_seqs = static_cast<int32_t>(num_seqs);
+    p.num_q_heads = static_cast<int32_t>(hq);
+    p.num_kv_heads = static_cast<int32_t>(hkv);
+    p.scale = scale;
+    p.causal = causal ? 1 : 0;
+    p.num_splits = 1;
+    return SINKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                 const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                 const sinkattn_tensor* cu_seqlens_q,
+                                 const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
+                                 const sinkattn_tensor* out, void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(out, "out", 3));
+    sinkattn::PrefillParams p{};
+    SA_TRY(check_prefill_inputs(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, p));
+    if (q->dtype == SINKATTN_F32) SA_TRY(check_dtype(out, "out", SINKATTN_F32));
+    else if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, "out: shape differs from q");
+    SA_TRY(check_data(out, "out"));
     SA_TRY(check_rows(out, "out"));
     SA_TRY(check_no_self_overlap(out, "out"));
     SA_TRY(check_disjoint(out, "out", q, "q"));
@@ -350,32 +380,64 @@ sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor
     SA_TRY(check_disjoint(out, "out", cu_seqlens_q, "cu_seqlens_q"));
     SA_TRY(check_disjoint(out, "out", cu_seqlens_k, "cu_seqlens_k"));
 
-    if (tq == 0 || num_seqs == 0) return SINKATTN_OK;
-
-    sinkattn::PrefillParams p{};
-    p.q = q->data;
-    p.k = k->data;
-    p.v = v->data;
-    p.sinks = static_cast<const float*>(sinks->data);
-    p.cu_seqlens_q = static_cast<const int32_t*>(cu_seqlens_q->data);
-    p.cu_seqlens_k = static_cast<const int32_t*>(cu_seqlens_k->data);
+    if (p.total_q == 0 || p.num_seqs == 0) return SINKATTN_OK;
     p.out = out->data;
-    p.q_stride_tok = q->stride[0];
-    p.q_stride_head = q->stride[1];
-    p.k_stride_tok = k->stride[0];
-    p.k_stride_head = k->stride[1];
-    p.v_stride_tok = v->stride[0];
-    p.v_stride_head = v->stride[1];
     p.o_stride_tok = out->stride[0];
     p.o_stride_head = out->stride[1];
-    p.total_q = tq;
-    p.total_k = tk;
-    p.num_seqs = static_cast<int32_t>(num_seqs);
-    p.num_q_heads = static_cast<int32_t>(hq);
-    p.num_kv_heads = static_cast<int32_t>(hkv);
-    p.scale = scale;
-    p.causal = causal ? 1 : 0;
     p.out_is_bf16 = out->dtype == SINKATTN_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_prefill_bf16(p, s)
+                                              : sinkattn::launch_prefill_f32(p, s));
+}
+
+sinkattn_status sinkattn_prefill_split(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                       const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                       const sinkattn_tensor* cu_seqlens_q,
+                                       const sinkattn_tensor* cu_seqlens_k, float scale,
+                                       int causal, int num_splits,
+                                       const sinkattn_tensor* partial_o,
+                                       const sinkattn_tensor* partial_m,
+                                       const sinkattn_tensor* partial_d, void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(partial_o, "partial_o", 4));
+    SA_TRY(check_desc(partial_m, "partial_m", 3));
+    SA_TRY(check_desc(partial_d, "partial_d", 3));
+    sinkattn::PrefillParams p{};
+    SA_TRY(check_prefill_inputs(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, p));
+    if (num_splits < 1 || num_splits > 65536)
+        return fail(SINKATTN_ERR_SHAPE, "num_splits must be in [1, 65536] (got %d)", num_splits);
+    SA_TRY(check_dtype(partial_o, "partial_o", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_m, "partial_m", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_d, "partial_d", SINKATTN_F32));
+    const int64_t want_o[4] = {q->shape[0], q->shape[1], num_splits, q->shape[2]};
+    for (int i = 0; i < 4; ++i)
+        if (partial_o->shape[i] != want_o[i])
+            return fail(SINKATTN_ERR_SHAPE, "partial_o: expected [Tq, Hq, num_splits, D]");
+    for (int i = 0; i < 3; ++i)
+        if (partial_m->shape[i] != want_o[i] || partial_d->shape[i] != want_o[i])
+            return fail(SINKATTN_ERR_SHAPE, "partial_m/partial_d: expected [Tq, Hq, num_splits]");
+    if (p.total_q * p.num_q_heads * static_cast<int64_t>(num_splits) >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "Tq * Hq * num_splits too large");
+    SA_TRY(check_data(partial_o, "partial_o"));
+    SA_TRY(check_data(partial_m, "partial_m"));
+    SA_TRY(check_data(partial_d, "partial_d"));
+    SA_TRY(check_contiguous(partial_o, "partial_o"));
+    SA_TRY(check_contiguous(partial_m, "partial_m"));
+    SA_TRY(check_contiguous(partial_d, "partial_d"));
+    const sinkattn_tensor* outs[3] = {partial_o, partial_m, partial_d};
+    const char* onames[3] = {"partial_o", "partial_m", "partial_d"};
+    const sinkattn_tensor* ins[6] = {q, k, v, sinks, cu_seqlens_q, cu_seqlens_k};
+    const char* inames[6] = {"q", "k", "v", "sinks", "cu_seqlens_q", "cu_seqlens_k"};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 6; ++b) SA_TRY(check_disjoint(outs[a], onames[a], ins[b], inames[b]));
+        for (int b = a + 1; b < 3; ++b) SA_TRY(check_disjoint(outs[a], onames[a], outs[b], onames[b]));
+    }
+
+    if (p.total_q == 0 || p.num_seqs == 0) return SINKATTN_OK;
+    p.num_splits = num_splits;
+    p.partial_o = static_cast<float*>(partial_o->data);
+    p.partial_m = static_cast<float*>(partial_m->data);
+    p.partial_d = static_cast<float*>(partial_d->data);
     hipStream_t s = static_cast<hipStream_t>(stream);
     return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_prefill_bf16(p, s)
                                               : sinkattn::launch_prefill_f32(p, s));

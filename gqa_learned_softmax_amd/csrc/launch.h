@@ -30,6 +30,13 @@ struct PrefillParams {
     float scale;
     int32_t causal;
     int32_t out_is_bf16;
+    // Split-KV prefill (sinkattn_prefill_split) when partial_o is not null: split j of a sequence
+    // covers keys [j * ks, min((j + 1) * ks, Lk)), ks = ceil(Lk / S) rounded up to 64; the state
+    // of (token t, head h, split j) goes to row (t * Hq + h) * S + j of the contiguous partials.
+    int32_t num_splits;
+    float* partial_o;
+    float* partial_m;
+    float* partial_d;
 };
 
 // Split-KV decode. q [B, Hq, D]; k/v [B, Lcap, Hkv, D]; partials contiguous.

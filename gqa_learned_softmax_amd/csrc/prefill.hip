@@ -85,6 +85,7 @@ __device__ bool locate_tile(const int32_t* cu_q, int num_seqs, int total_q, int 
     return false;
 }
 
+template <bool kSplit>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillParams p) {
     __shared__ __attribute__((aligned(16))) __bf16 k_tile[2][kKeyTile][kKPitch];
     __shared__ __attribute__((aligned(16))) __bf16 v_tile[2][kKeyTile][kVPitch];
@@ -95,8 +96,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     const int col = lane & 31;   // MFMA column: query row within a 32-row block
     const int half = lane >> 5;  // k-slot group
 
-    const int g = blockIdx.x % p.num_kv_heads;
-    const int tile = blockIdx.x / p.num_kv_heads;
+    // Work-group order: KV head fastest, then (split-KV prefill) the split, then the query tile.
+    int bid = blockIdx.x;
+    const int g = bid % p.num_kv_heads;
+    bid /= p.num_kv_heads;
+    int split = 0;
+    if constexpr (kSplit) {
+        split = bid % p.num_splits;
+        bid /= p.num_splits;
+    }
+    const int tile = bid;
     const int group = p.num_q_heads / p.num_kv_heads;
     const int positions_per_tile = kRowsPerTile / group;
 
@@ -140,6 +149,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     const int safe_end = p.causal ? min(k_len, first_pos + offset + 1) : k_len;
     const int num_tiles = (key_end + kKeyTile - 1) / kKeyTile;
     const int mask_from = min(num_tiles, max(safe_end, 0) / kKeyTile);
+    // KV tiles of this work-group: all of them, or (split-KV prefill) those of its split, whose
+    // boundaries fall on whole tiles except at the sequence end. Only split 0 carries the sink.
+    int kt_begin = 0, kt_end = num_tiles;
+    bool carries_sink = true;
+    if constexpr (kSplit) {
+        const int per = (k_len + p.num_splits - 1) / p.num_splits;
+        const int split_keys = (per + kKeyTile - 1) / kKeyTile * kKeyTile;
+        const int lo = min(split * split_keys, k_len);
+        const int hi = min(lo + split_keys, k_len);
+        // A non-empty split starts at split * split_keys < Lk, a whole tile; an empty one (lo
+        // clamped to Lk, which may fall inside a tile) processes no tile at all.
+        kt_begin = lo / kKeyTile;
+        kt_end = hi > lo ? max(kt_begin, min(num_tiles, (hi + kKeyTile - 1) / kKeyTile)) : kt_begin;
+        carries_sink = split == 0;
+    }
 
     // K/V rows [0, key_end) of KV head g of this sequence; loads past the end return zeros.
     const __bf16* kbase = static_cast<const __bf16*>(p.k) + static_cast<int64_t>(k_start) * p.k_stride_tok +
@@ -416,26 +440,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         constexpr bool kAllowFast = decltype(allow_fast_tag)::value;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            // Sink fold: m starts at the head's sink, d at 1 (kept in the half-0 lane's share).
-            m[cb] = sink2[cb];
+            // Sink fold: m starts at the head's sink, d at 1 (kept in the half-0 lane's share);
+            // a split other than the first starts empty (m = -inf, d = 0).
+            m[cb] = carries_sink ? sink2[cb] : kNegInf;
             dsum[cb] = (half == 0 && m[cb] != kNegInf) ? 1.0f : 0.0f;
 #pragma unroll
             for (int n = 0; n < 2; ++n) acc[cb][n] = zero_f32x16();
         }
-        if (num_tiles > 0) {
-            fetch(0);
-            stash(0);
+        if (kt_begin < kt_end) {
+            fetch(kt_begin * kKeyTile);
+            stash(kt_begin & 1);
         }
         __syncthreads();
-        int kt = 0;
-        for (; kt < mask_from; ++kt) {
+        const int unmasked_end = min(mask_from, kt_end);
+        int kt = kt_begin;
+        for (; kt < unmasked_end; ++kt) {
             if (kAllowFast && wave_zero_ref()) break;
             plain_tile(kt, False(), False(), allow_fast_tag);
         }
         if constexpr (kAllowFast) {
-            for (; kt < mask_from; ++kt) fast_tile(kt);
+            for (; kt < unmasked_end; ++kt) fast_tile(kt);
         }
-        for (; kt < num_tiles; ++kt) {
+        for (; kt < kt_end; ++kt) {
             if (kAllowFast && wave_zero_ref())
                 plain_tile(kt, True(), True(), False());
             else
@@ -465,11 +491,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     if (redo_general) process(False());
 
     // Epilogue: out = acc / d. Lane holds d-channels 32n + 8 (r / 4) + 4 half + r % 4.
+    // Split-KV prefill writes the split's state instead: o = acc / d, m (natural log), d.
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const float dtot = sum_xor32(dsum[cb]);
         if (!valid[cb]) continue;
         const float inv = dtot > 0.0f ? 1.0f / dtot : 0.0f;
+        if constexpr (kSplit) {
+            const int64_t row = (static_cast<int64_t>(q_start + pos[cb]) * p.num_q_heads + head[cb]) * p.num_splits + split;
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int quad = 0; quad < 4; ++quad) {
+                    f32x4 o;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = acc[cb][n][4 * quad + i] * inv;
+                    *reinterpret_cast<f32x4*>(p.partial_o + row * kHeadDim + 32 * n + 8 * quad + 4 * half) = o;
+                }
+            if (half == 0) {
+                p.partial_m[row] = dtot > 0.0f ? m[cb] * kLn2 : kNegInf;
+                p.partial_d[row] = dtot;
+            }
+            continue;
+        }
         const int64_t obase = static_cast<int64_t>(q_start + pos[cb]) * p.o_stride_tok +
                               static_cast<int64_t>(head[cb]) * p.o_stride_head;
 #pragma unroll
@@ -522,33 +566,56 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
     const float* qrow = static_cast<const float*>(p.q) + static_cast<int64_t>(tok) * p.q_stride_tok +
                         static_cast<int64_t>(head) * p.q_stride_head;
     float qv[kHeadDim], acc[kHeadDim];
-    for (int d = 0; d < kHeadDim; ++d) {
-        qv[d] = qrow[d];
-        acc[d] = 0.0f;
-    }
-    float m = p.sinks[head];
-    float dsum = m == kNegInf ? 0.0f : 1.0f;
+    for (int d = 0; d < kHeadDim; ++d) qv[d] = qrow[d];
     const float* kb = static_cast<const float*>(p.k) + static_cast<int64_t>(k_start) * p.k_stride_tok +
                       static_cast<int64_t>(g) * p.k_stride_head;
     const float* vb = static_cast<const float*>(p.v) + static_cast<int64_t>(k_start) * p.v_stride_tok +
                       static_cast<int64_t>(g) * p.v_stride_head;
-    for (int j = 0; j < key_end; ++j) {
-        const float* kr = kb + static_cast<int64_t>(j) * p.k_stride_tok;
-        const float* vr = vb + static_cast<int64_t>(j) * p.v_stride_tok;
-        float s = 0.0f;
-        for (int d = 0; d < kHeadDim; ++d) s = fmaf(qv[d], kr[d], s);
-        s *= p.scale;
-        if (s > m) {
-            const float alpha = m == kNegInf ? 0.0f : expf(m - s);
-            dsum = dsum * alpha + 1.0f;
-            for (int d = 0; d < kHeadDim; ++d) acc[d] = acc[d] * alpha + vr[d];
-            m = s;
-        } else {
-            const float pj = expf(s - m);
-            dsum += pj;
-            for (int d = 0; d < kHeadDim; ++d) acc[d] = fmaf(pj, vr[d], acc[d]);
+    // Keys [j0, j1) folded into (m, dsum, acc) with the page's recurrence.
+    float m, dsum;
+    auto fold = [&](int j0, int j1) {
+        for (int j = j0; j < j1; ++j) {
+            const float* kr = kb + static_cast<int64_t>(j) * p.k_stride_tok;
+            const float* vr = vb + static_cast<int64_t>(j) * p.v_stride_tok;
+            float s = 0.0f;
+            for (int d = 0; d < kHeadDim; ++d) s = fmaf(qv[d], kr[d], s);
+            s *= p.scale;
+            if (s > m) {
+                const float alpha = m == kNegInf ? 0.0f : expf(m - s);
+                dsum = dsum * alpha + 1.0f;
+                for (int d = 0; d < kHeadDim; ++d) acc[d] = acc[d] * alpha + vr[d];
+                m = s;
+            } else {
+                const float pj = expf(s - m);
+                dsum += pj;
+                for (int d = 0; d < kHeadDim; ++d) acc[d] = fmaf(pj, vr[d], acc[d]);
+            }
         }
+    };
+    auto start = [&](bool with_sink) {
+        m = with_sink ? p.sinks[head] : kNegInf;
+        dsum = m == kNegInf ? 0.0f : 1.0f;
+        for (int d = 0; d < kHeadDim; ++d) acc[d] = 0.0f;
+    };
+    if (p.partial_o != nullptr) {
+        // Split-KV prefill: every split of this row in turn (boundaries as in the bf16 kernel).
+        const int per = (k_len + p.num_splits - 1) / p.num_splits;
+        const int split_keys = (per + 63) / 64 * 64;
+        for (int sp = 0; sp < p.num_splits; ++sp) {
+            const int lo = min(sp * split_keys, k_len);
+            const int hi = min(lo + split_keys, key_end);
+            start(sp == 0);
+            fold(lo, hi);
+            const int64_t row = (static_cast<int64_t>(tok) * p.num_q_heads + head) * p.num_splits + sp;
+            const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;
+            for (int d = 0; d < kHeadDim; ++d) p.partial_o[row * kHeadDim + d] = acc[d] * inv;
+            p.partial_m[row] = dsum > 0.0f ? m : kNegInf;
+            p.partial_d[row] = dsum;
+        }
+        return;
     }
+    start(true);
+    fold(0, key_end);
     const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;
     float* orow = static_cast<float*>(p.out) + static_cast<int64_t>(tok) * p.o_stride_tok +
                   static_cast<int64_t>(head) * p.o_stride_head;
@@ -563,9 +630,13 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
     // Upper bound on query tiles without reading cu_seqlens: each sequence adds at most one
     // partial tile beyond ceil(Tq / positions_per_tile).
     const int64_t tiles = (p.total_q + positions_per_tile - 1) / positions_per_tile + p.num_seqs;
-    const int64_t blocks = tiles * p.num_kv_heads;
+    const bool split = p.partial_o != nullptr;
+    const int64_t blocks = tiles * p.num_kv_heads * (split ? p.num_splits : 1);
     if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
-    prefill_bf16_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kPfThreads), 0, stream>>>(p);
+    if (split)
+        prefill_bf16_kernel<true><<<dim3(static_cast<unsigned>(blocks)), dim3(kPfThreads), 0, stream>>>(p);
+    else
+        prefill_bf16_kernel<false><<<dim3(static_cast<unsigned>(blocks)), dim3(kPfThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 

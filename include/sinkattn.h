@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_VERSION 2
+#define SINKATTN_VERSION 3
 
 typedef enum {
     SINKATTN_OK = 0,
@@ -104,6 +104,34 @@ sinkattn_status sinkattn_prefill(const sinkattn_tensor* q, const sinkattn_tensor
                                  const sinkattn_tensor* cu_seqlens_q,
                                  const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
                                  const sinkattn_tensor* out, void* stream);
+
+/*
+ * sinkattn_prefill_split - varlen prefill split along each sequence's KV length.
+ *
+ * Source: "GPT-OSS on Day 0", "Sink attention" subsection: when attention is split into chunks
+ * along the KV length, the sink is folded into the first chunk only; the same rule applied to
+ * prefill. Meant for prefills whose query tiles alone cannot fill the GPU (a few hundred new tokens
+ * against a long cache): each (query tile, KV head, split) is its own work-group. The partials
+ * use the decode format, and sinkattn_decode_merge with partial_o viewed as [Tq, Hq, S, D]
+ * ("batch" = Tq) combines them into the sinkattn_prefill result (equal up to rounding).
+ *
+ *   q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal: as for sinkattn_prefill
+ *   num_splits   S >= 1. Split j of sequence b covers its keys [j*ks, min((j+1)*ks, Lk_b)),
+ *                ks = ceil(Lk_b / S) rounded up to a multiple of 64; splits past the end are empty.
+ *   partial_o    [Tq, Hq, S, D] fp32 contiguous   o = the split's softmax-weighted mean of V
+ *   partial_m    [Tq, Hq, S]    fp32 contiguous   m = a reference logit of the split (natural log)
+ *   partial_d    [Tq, Hq, S]    fp32 contiguous   d = sum of e^(term - m) over the split's terms
+ * A row's state in a split covers the keys of the split it may see (causal rule as above), plus
+ * the sink in split 0. A split with no such term is (o, m, d) = (0, -inf, 0).
+ */
+sinkattn_status sinkattn_prefill_split(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                       const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                       const sinkattn_tensor* cu_seqlens_q,
+                                       const sinkattn_tensor* cu_seqlens_k, float scale,
+                                       int causal, int num_splits,
+                                       const sinkattn_tensor* partial_o,
+                                       const sinkattn_tensor* partial_m,
+                                       const sinkattn_tensor* partial_d, void* stream);
 
 /*
  * sinkattn_decode_split - one query token per sequence against a padded KV cache, split along the

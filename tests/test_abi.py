@@ -142,6 +142,55 @@ def test_prefill_f32_inputs_need_f32_out():
     assert call_prefill(prefill_args(tq=0, out_dtype=F32)) == _lib.OK
 
 
+# ----------------------------------------------------------------------------- prefill_split
+def psplit_args(tq=16, hq=8, hkv=2, dim=64, b=1, splits=3, dtype=BF16):
+    a = prefill_args(tq=tq, hq=hq, hkv=hkv, dim=dim, b=b, dtype=dtype)
+    del a["out"]
+    a.update(splits=splits, po=T([tq, hq, splits, dim], F32), pm=T([tq, hq, splits], F32),
+             pd=T([tq, hq, splits], F32))
+    return a
+
+
+def call_psplit(a):
+    return _lib.lib.sinkattn_prefill_split(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]), R(a["cu_q"]),
+                                           R(a["cu_k"]), a["scale"], a["causal"], a["splits"], R(a["po"]),
+                                           R(a["pm"]), R(a["pd"]), None)
+
+
+def test_prefill_split_empty_batch_is_ok():
+    assert call_psplit(psplit_args(tq=0)) == _lib.OK
+    assert call_psplit(psplit_args(tq=0, b=0)) == _lib.OK
+
+
+PSPLIT_CASES = [
+    ("po_null", lambda a: _mut(a, po=None), _lib.ERR_NULL),
+    ("pd_null", lambda a: _mut(a, pd=None), _lib.ERR_NULL),
+    ("q_null", lambda a: _mut(a, q=None), _lib.ERR_NULL),
+    ("partial_bf16", lambda a: _mut(a, po=T([16, 8, 3, 64], BF16)), _lib.ERR_DTYPE),
+    ("k_dtype_mismatch", lambda a: _mut(a, k=T([16, 2, 64], F32)), _lib.ERR_DTYPE),
+    ("splits_zero", lambda a: _mut(a, splits=0), _lib.ERR_SHAPE),
+    ("splits_negative", lambda a: _mut(a, splits=-2), _lib.ERR_SHAPE),
+    ("splits_mismatch", lambda a: _mut(a, splits=4), _lib.ERR_SHAPE),
+    ("po_tokens", lambda a: _mut(a, po=T([15, 8, 3, 64], F32)), _lib.ERR_SHAPE),
+    ("pm_shape", lambda a: _mut(a, pm=T([16, 8, 2], F32)), _lib.ERR_SHAPE),
+    ("po_rank3", lambda a: _mut(a, po=T([16, 8, 192], F32)), _lib.ERR_SHAPE),
+    ("scale_nan", lambda a: _mut(a, scale=float("nan")), _lib.ERR_SHAPE),
+    ("head_dim_128", lambda a: psplit_args(dim=128), _lib.ERR_UNSUPPORTED),
+    ("group_3", lambda a: psplit_args(hq=6, hkv=2), _lib.ERR_UNSUPPORTED),
+    ("po_strided", lambda a: _mut(a, po=T([16, 8, 3, 64], F32, strides=[4096, 256, 64, 1])), _lib.ERR_LAYOUT),
+    ("pm_overlaps_pd", lambda a: _mut(a, pm=T([16, 8, 3], F32, addr=a["pd"].data + 4)), _lib.ERR_LAYOUT),
+    ("po_overlaps_q", lambda a: _mut(a, po=T([16, 8, 3, 64], F32, addr=a["q"].data + 256)), _lib.ERR_LAYOUT),
+    ("pd_overlaps_cu", lambda a: _mut(a, pd=T([16, 8, 3], F32, addr=a["cu_k"].data)), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", PSPLIT_CASES, ids=[c[0] for c in PSPLIT_CASES])
+def test_prefill_split_rejects(name, mutate, code):
+    status = call_psplit(mutate(psplit_args()))
+    assert status == code, (status, last_error())
+    assert last_error()
+
+
 # ----------------------------------------------------------------------------- decode_split
 def split_args(b=2, hq=8, hkv=1, cap=64, chunks=4, dim=64, dtype=BF16):
     return dict(q=T([b, hq, dim], dtype), k=T([b, cap, hkv, dim], dtype), v=T([b, cap, hkv, dim], dtype),

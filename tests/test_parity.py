@@ -186,6 +186,97 @@ def test_prefill_bf16_logits_grow_after_early_keys(factor, causal):
     check_bf16(out, ref, f"prefill keys x{factor}")
 
 
+# ----------------------------------------------------------------------------- split-KV prefill
+PREFILL_SPLIT_CASES = [
+    # (name, lens_q, lens_k, Hq, Hkv, causal, splits)
+    ("append_long_kv", [100], [2000], 64, 8, True, 4),
+    ("varlen_causal", [300, 77, 0, 129], None, 64, 8, True, 3),
+    ("noncausal", [90, 130], None, 64, 8, False, 5),
+    ("more_splits_than_tiles", [70], [300], 64, 8, True, 40),
+    ("one_split", [200], None, 64, 8, True, 1),
+    ("group16_append", [33, 5], [700, 64], 64, 4, True, 6),
+]
+
+
+def _check_split_states(po, pm, pd, rpo, rpm, rpd, label):
+    """States are unique up to their reference logit: compare o and m + ln d (the log-weight).
+    The prefill row sum is taken on bf16-rounded P (relative error <= 2^-9 per term), so the
+    log-weight is compared to 5e-3."""
+    gpo, gpm, gpd = _np(po), _np(pm), _np(pd)
+    ref_live, live = rpd > 0, gpd > 0
+    assert np.array_equal(ref_live, live), f"{label}: empty splits differ"
+    assert np.all(np.isneginf(gpm[~live])), f"{label}: empty split with finite m"
+    lw, rlw = gpm[live] + np.log(gpd[live]), rpm[ref_live] + np.log(rpd[ref_live])
+    np.testing.assert_allclose(lw, rlw, atol=5e-3, err_msg=f"{label}: log-weight")
+    check_bf16(torch.from_numpy(np.where(live[..., None], gpo, 0.0)),
+               np.where(ref_live[..., None], rpo, 0.0), f"{label} o")
+
+
+@pytest.mark.parametrize("name,lq,lk,hq,hkv,causal,splits", PREFILL_SPLIT_CASES,
+                         ids=[c[0] for c in PREFILL_SPLIT_CASES])
+def test_prefill_split_bf16(name, lq, lk, hq, hkv, causal, splits):
+    sa = _sa()
+    case = workloads.make_prefill(lq, lk, num_q_heads=hq, num_kv_heads=hkv, seed=_seed(name), causal=causal)
+    q, k, v, sinks, cq, ck = _dev(case.q, case.k, case.v, case.sinks, case.cu_seqlens_q, case.cu_seqlens_k)
+    po, pm, pd = sa.prefill_split(q, k, v, sinks, cq, ck, case.scale, causal, splits)
+    torch.cuda.synchronize()
+    rpo, rpm, rpd = oracle.prefill_split(_np(case.q), _np(case.k), _np(case.v), _np(case.sinks),
+                                         case.cu_seqlens_q.numpy(), case.cu_seqlens_k.numpy(), case.scale,
+                                         causal, splits)
+    _check_split_states(po, pm, pd, rpo, rpm, rpd, f"prefill_split {name}")
+    out = sa.prefill_kv_split(q, k, v, sinks, cq, ck, case.scale, causal, splits)
+    torch.cuda.synchronize()
+    ref, _ = oracle_prefill(case)
+    check_bf16(out, ref, f"prefill_kv_split {name}")
+
+
+def test_prefill_split_logits_overflow_recompute():
+    """Later keys x32: zero-reference tiles overflow, the work-group recomputes; per split too."""
+    sa = _sa()
+    case = workloads.make_prefill([300], [1200], num_q_heads=64, num_kv_heads=8, seed=77)
+    case.k[256:] *= 32.0
+    q, k, v, sinks, cq, ck = _dev(case.q, case.k, case.v, case.sinks, case.cu_seqlens_q, case.cu_seqlens_k)
+    out = sa.prefill_kv_split(q, k, v, sinks, cq, ck, case.scale, True, 3)
+    torch.cuda.synchronize()
+    ref, _ = oracle_prefill(case)
+    check_bf16(out, ref, "prefill_kv_split keys x32")
+
+
+def test_prefill_split_fp32_tiny():
+    sa = _sa()
+    pre = workloads.make(1).prefill
+    q, k, v, sinks, cq, ck = _dev(pre.q, pre.k, pre.v, pre.sinks, pre.cu_seqlens_q, pre.cu_seqlens_k)
+    po, pm, pd = sa.prefill_split(q, k, v, sinks, cq, ck, pre.scale, True, 3)
+    torch.cuda.synchronize()
+    rpo, rpm, rpd = oracle.prefill_split(_np(pre.q), _np(pre.k), _np(pre.v), _np(pre.sinks),
+                                         pre.cu_seqlens_q.numpy(), pre.cu_seqlens_k.numpy(), pre.scale, True, 3)
+    gpd = _np(pd)
+    assert np.array_equal(gpd > 0, rpd > 0)
+    live = rpd > 0
+    np.testing.assert_allclose(_np(pm)[live] + np.log(gpd[live]), rpm[live] + np.log(rpd[live]), rtol=1e-6)
+    out = sa.prefill_kv_split(q, k, v, sinks, cq, ck, pre.scale, True, 3)
+    torch.cuda.synchronize()
+    ref, _ = oracle_prefill(pre)
+    check_f32(out, ref, "prefill_kv_split tiny f32")
+
+
+def test_prefill_split_append_32k_sampled_rows():
+    """Chunked prefill of 512 new tokens against a 32768-key cache (64/8 heads), 8 splits:
+    sampled rows against the oracle row by row."""
+    sa = _sa()
+    case = workloads.make_prefill([512], [32768], num_q_heads=64, num_kv_heads=8, seed=4321)
+    q, k, v, sinks, cq, ck = _dev(case.q, case.k, case.v, case.sinks, case.cu_seqlens_q, case.cu_seqlens_k)
+    out = sa.prefill_kv_split(q, k, v, sinks, cq, ck, case.scale, True, 8)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    tokens = np.concatenate([[0, 511], rng.integers(0, 512, 14)])
+    heads = rng.integers(0, 64, tokens.size)
+    ref, _ = oracle.prefill_at(_np(case.q), _np(case.k), _np(case.v), _np(case.sinks), case.cu_seqlens_q.numpy(),
+                               case.cu_seqlens_k.numpy(), case.scale, True, tokens, heads)
+    got = torch.from_numpy(_np(out)[tokens, heads])
+    check_bf16(got, ref, "prefill_kv_split append 512 x 32768 (sampled)")
+
+
 def test_prefill_bf16_sink_neg_inf_is_plain_attention():
     sa = _sa()
     case = workloads.make_prefill([130, 64], num_q_heads=64, num_kv_heads=8, seed=7)

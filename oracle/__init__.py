@@ -11,6 +11,8 @@ from .sink_attention import (  # noqa: F401
     chunk_size,
     chunk_state,
     decode,
+    decode_multi,
+    decode_multi_split,
     decode_split,
     merge,
     online_row,

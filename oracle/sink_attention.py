@@ -228,6 +228,62 @@ def decode_split(q, k, v, sinks, seqlens_k, num_chunks, scale):
     return po, pm, pd
 
 
+def decode_multi(q, k, v, sinks, seqlens_k, scale):
+    """Multi-token decode: the last T rows of each sequence, against a KV cache that holds them.
+
+    q [B, T, Hq, D]; k, v [B, Lcap, Hkv, D]; seqlens_k [B] counts the T new tokens. Token t of
+    sequence b is query row t of a block of T queries against L = seqlens_k[b] keys, under the
+    bottom-right causal rule: it sees keys j <= L - T + t.
+    Returns ``(out [B, T, Hq, D], lse [B, T, Hq])``.
+    """
+    q, sinks = _f64(q), _f64(sinks)
+    batch, q_len, h_q, dim = q.shape
+    group = _group(h_q, k.shape[2])
+    out = np.zeros((batch, q_len, h_q, dim))
+    lse = np.full((batch, q_len, h_q), NEG_INF)
+    for b in range(batch):
+        n = int(seqlens_k[b])
+        allowed = causal_allowed(np.arange(q_len), q_len, n)
+        for h in range(h_q):
+            g = h // group
+            o, l = attend(q[b, :, h], _f64(k[b, :n, g]), _f64(v[b, :n, g]), sinks[h], scale, allowed)
+            out[b, :, h], lse[b, :, h] = o, l
+    return out, lse
+
+
+def decode_multi_split(q, k, v, sinks, seqlens_k, num_chunks, scale):
+    """Split-KV partials of multi-token decode, by the chunk definition.
+
+    Chunk ``c`` covers keys ``[c*cs, (c+1)*cs)``, cs = ceil(Lcap / C), intersected with the keys
+    token t may see (``j <= L - T + t``); chunk 0 carries the sink. Row ``b*T + t`` of the
+    partials holds token t of sequence b: ``(partial_o [B*T, Hq, C, D], partial_m [B*T, Hq, C],
+    partial_d [B*T, Hq, C])``.
+    """
+    q, sinks = _f64(q), _f64(sinks)
+    batch, q_len, h_q, dim = q.shape
+    cap = k.shape[1]
+    group = _group(h_q, k.shape[2])
+    cs = chunk_size(cap, num_chunks)
+    po = np.zeros((batch * q_len, h_q, num_chunks, dim))
+    pm = np.full((batch * q_len, h_q, num_chunks), NEG_INF)
+    pd = np.zeros((batch * q_len, h_q, num_chunks))
+    for b in range(batch):
+        n = int(seqlens_k[b])
+        for t in range(q_len):
+            seen = max(0, min(n, n - q_len + 1 + t))  # keys 0 .. seen - 1
+            for h in range(h_q):
+                g = h // group
+                for c in range(num_chunks):
+                    lo, hi = c * cs, min((c + 1) * cs, seen)
+                    keys = _f64(k[b, lo:hi, g]) if hi > lo else np.zeros((0, dim))
+                    vals = _f64(v[b, lo:hi, g]) if hi > lo else np.zeros((0, dim))
+                    z = scale * (keys @ q[b, t, h])
+                    m, d, o = chunk_state(z, vals, sinks[h] if c == 0 else None)
+                    row = b * q_len + t
+                    po[row, h, c], pm[row, h, c], pd[row, h, c] = o, m, d
+    return po, pm, pd
+
+
 def split_size(num_keys: int, num_splits: int, align: int = 64) -> int:
     """Keys per KV split of one prefill sequence: ceil(Lk / S) rounded up to a multiple of ``align``.
 

@@ -490,3 +490,93 @@ def test_zero_length_and_dead_rows_are_zero():
     out, lse = oracle.decode(q, k, k, [1.0, float("-inf")], [0], 0.125)
     assert np.all(out == 0)
     assert lse[0, 0] == 1.0 and lse[0, 1] == float("-inf")
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+def _multi_case(batch, q_len, cap, lens, h_q, h_kv, seed):
+    q = _rand((batch, q_len, h_q, D), seed)
+    k = _rand((batch, cap, h_kv, D), seed + 1)
+    v = _rand((batch, cap, h_kv, D), seed + 2)
+    sinks = _rand(h_q, seed + 3) * 2
+    return q, k, v, sinks, np.asarray(lens, dtype=np.int32)
+
+
+def test_decode_multi_is_sdpa_with_a_sink_key_and_bottom_right_mask():
+    """Each sequence: SDPA (float64 library routine) over [K; 0], [V; 0] with additive mask
+    [bottom-right causal | sink_h], the KV heads repeated over their query-head groups."""
+    q, k, v, sinks, lens = _multi_case(3, 5, 21, [21, 9, 6], 8, 2, 700)
+    out, lse = oracle.decode_multi(q, k, v, sinks, lens, 0.125)
+    for b, n in enumerate(lens):
+        kb = np.repeat(k[b, :n], 4, axis=1)  # [n, Hq, D]
+        vb = np.repeat(v[b, :n], 4, axis=1)
+        k_aug = np.concatenate([kb, np.zeros((1, 8, D))], axis=0).transpose(1, 0, 2)[None].copy()
+        v_aug = np.concatenate([vb, np.zeros((1, 8, D))], axis=0).transpose(1, 0, 2)[None].copy()
+        mask = np.zeros((1, 8, 5, n + 1))
+        for t in range(5):
+            mask[0, :, t, n - 5 + t + 1:n] = -np.inf  # token t sees keys j <= n - 5 + t
+        mask[..., n] = sinks[None, :, None]
+        ref = _sdpa(q[b].transpose(1, 0, 2)[None].copy(), k_aug, v_aug, 0.125, mask=mask)
+        np.testing.assert_allclose(out[b], ref[0].transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+    assert np.all(np.isfinite(lse))
+
+
+def test_decode_multi_rows_equal_prefill_of_the_last_rows():
+    """Token t of a sequence of L keys is prefill row t of Lq = T queries against Lk = L keys."""
+    q, k, v, sinks, lens = _multi_case(2, 4, 30, [30, 11], 4, 4, 710)
+    out, lse = oracle.decode_multi(q, k, v, sinks, lens, 0.2)
+    for b, n in enumerate(lens):
+        pre, pre_lse = oracle.prefill(q[b], k[b, :n], v[b, :n], sinks, [0, 4], [0, n], 0.2, causal=True)
+        np.testing.assert_allclose(out[b], pre, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lse[b], pre_lse, rtol=1e-13)
+
+
+def test_decode_multi_with_one_token_is_decode():
+    q, k, v, sinks, lens = _multi_case(3, 1, 17, [17, 4, 0], 8, 2, 720)
+    out, lse = oracle.decode_multi(q, k, v, sinks, lens, 0.125)
+    ref, ref_lse = oracle.decode(q[:, 0], k, v, sinks, lens, 0.125)
+    np.testing.assert_allclose(out[:, 0], ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse[:, 0], ref_lse, rtol=1e-14)
+    po, pm, pd = oracle.decode_multi_split(q, k, v, sinks, lens, 3, 0.125)
+    so, sm, sd = oracle.decode_split(q[:, 0], k, v, sinks, lens, 3, 0.125)
+    np.testing.assert_array_equal(po, so)
+    np.testing.assert_array_equal(pm, sm)
+    np.testing.assert_array_equal(pd, sd)
+
+
+def test_decode_multi_rows_without_keys_put_all_weight_on_the_sink():
+    """With fewer keys than tokens, token t sees L - T + 1 + t <= 0 keys: out = 0, lse = sink."""
+    q, k, v, sinks, lens = _multi_case(1, 6, 8, [3], 2, 1, 730)
+    out, lse = oracle.decode_multi(q, k, v, sinks, lens, 0.125)
+    for t in range(3):  # 3 - 6 + 1 + t <= 0 for t <= 2
+        np.testing.assert_array_equal(out[0, t], np.zeros((2, D)))
+        np.testing.assert_allclose(lse[0, t], sinks, rtol=1e-15)
+    assert np.all(np.abs(out[0, 3:]) > 0)
+
+
+@pytest.mark.parametrize("chunks", [1, 2, 3, 5, 8, 40])
+def test_decode_multi_split_merge_equals_unsplit(chunks):
+    """Chunk borders fall inside the masked last T - 1 keys for some chunkings; lengths below T
+    leave rows with no keys."""
+    q, k, v, sinks, lens = _multi_case(4, 5, 40, [40, 23, 5, 2], 8, 4, 740)
+    ref, ref_lse = oracle.decode_multi(q, k, v, sinks, lens, 0.125)
+    po, pm, pd = oracle.decode_multi_split(q, k, v, sinks, lens, chunks, 0.125)
+    out, lse = oracle.merge(po, pm, pd)
+    np.testing.assert_allclose(out.reshape(ref.shape), ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse.reshape(ref_lse.shape), ref_lse, rtol=1e-12)
+
+
+def test_decode_multi_split_mutation_sink_in_every_chunk_is_caught():
+    q, k, v, sinks, lens = _multi_case(1, 3, 24, [24], 2, 1, 750)
+    ref, _ = oracle.decode_multi(q, k, v, sinks, lens, 0.125)
+    po, pm, pd = oracle.decode_multi_split(q, k, v, sinks, lens, 4, 0.125)
+    cs = oracle.chunk_size(24, 4)
+    for t in range(3):
+        seen = 24 - 3 + 1 + t
+        for h in range(2):
+            for c in range(1, 4):
+                lo, hi = c * cs, min((c + 1) * cs, seen)
+                z = 0.125 * (k[0, lo:hi, 0] @ q[0, t, h])
+                m, d, o = oracle.chunk_state(z, v[0, lo:hi, 0], sinks[h])
+                po[t, h, c], pm[t, h, c], pd[t, h, c] = o, m, d
+    out, _ = oracle.merge(po, pm, pd)
+    assert np.max(np.abs(out.reshape(ref.shape) - ref)) > 1e-3

@@ -16,10 +16,12 @@ The same JSON line also carries:
   allowed causal pairs (4 * D per pair) against the 2.5 PFLOP/s dense bf16 MFMA peak;
 * ``prefill_append``: 512 new tokens against a 32768-key cache, unsplit and split 4 ways along the
   KV length (sinkattn_prefill_split + sinkattn_decode_merge);
+* ``decode_multi``: the decode workload with T = 2, 4, 8 new tokens per sequence (the last T of the
+  8192 keys), split + merge and single-launch, in KV GB/s;
 * ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
-                      [--no-hot]
+                      [--no-hot] [--no-multi]
 """
 from __future__ import annotations
 
@@ -141,6 +143,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode detail")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the steps that reuse one K/V set (cache-resident; never the headline)")
     args = ap.parse_args()
@@ -305,6 +308,41 @@ def main():
             "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         },
     }
+
+    # ---------------------------------------------------------------- multi-token decode (detail)
+    if not args.no_multi:
+        multi = {"workload": "decode_multi_b8_hq64_hkv8_d64_len8192_chunks8", "tokens": {}}
+        gen = torch.Generator().manual_seed(1007)
+        for t in (2, 4, 8):
+            qm = torch.randn((batch, t, hq, dim), generator=gen).to(torch.bfloat16).to(dev)
+            mpo = torch.empty((batch * t, hq, chunks, dim), dtype=torch.float32, device=dev)
+            mpm = torch.empty((batch * t, hq, chunks), dtype=torch.float32, device=dev)
+            mpd = torch.empty_like(mpm)
+            mout = torch.empty((batch, t, hq, dim), dtype=torch.bfloat16, device=dev)
+            mws = sa.decode_workspace(batch * t, hq, case.k.shape[2], chunks, dev)
+
+            def m_split_merge(i, qm=qm, mpo=mpo, mpm=mpm, mpd=mpd, mout=mout):
+                sa.decode_multi_split(qm, ks[i % n_sets], vs[i % n_sets], sinks, seqlens, chunks, case.scale,
+                                      mpo, mpm, mpd)
+                sa.decode_merge(mpo, mpm, mpd, out=mout.view(batch * t, hq, dim))
+
+            def m_fused(i, qm=qm, mws=mws, mout=mout):
+                sa.decode_multi_fused(qm, ks[i % n_sets], vs[i % n_sets], sinks, seqlens, chunks, case.scale,
+                                      mws, out=mout)
+
+            m_split_merge(0)
+            m_fused(0)
+            ms_m2 = _time_graph(_capture(m_split_merge, n_rep, torch), n_rep, torch)
+            ms_mf = _time_graph(_capture(m_fused, n_rep, torch), n_rep, torch)
+            m_bytes = kv_bytes + 2 * qm.numel() * 2 + case.sinks.numel() * 4
+            multi["tokens"][str(t)] = {
+                "split_plus_merge_us": round(ms_m2 * 1e3, 3), "fused_us": round(ms_mf * 1e3, 3),
+                "split_plus_merge_gbs": round(m_bytes / (ms_m2 * 1e-3) / 1e9, 1),
+                "fused_gbs": round(m_bytes / (ms_mf * 1e-3) / 1e9, 1),
+            }
+            _log(f"multi-token decode T={t}: split+merge {ms_m2 * 1e3:.2f} us, fused {ms_mf * 1e3:.2f} us "
+                 f"({m_bytes / (ms_mf * 1e-3) / 1e9:.0f} GB/s)")
+        result["decode_multi"] = multi
     del ks, vs, k0, v0
 
     # ---------------------------------------------------------------- prefill (second half of metric)

@@ -15,7 +15,8 @@ from . import _lib
 from ._lib import SinkAttnError  # noqa: F401
 
 __all__ = ["prefill", "prefill_split", "prefill_kv_split", "decode_split", "decode_merge", "decode",
-           "decode_fused", "decode_workspace", "SinkAttnError", "version"]
+           "decode_fused", "decode_workspace", "decode_multi_split", "decode_multi", "decode_multi_fused",
+           "SinkAttnError", "version"]
 
 
 def version() -> int:
@@ -119,6 +120,56 @@ def decode_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, out=No
     dev = _lib.require_device(q, k, v, sinks, seqlens_k, workspace, out, lse)
     d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k, out, lse)]
     _lib.check(_lib.lib.sinkattn_decode(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        int(num_chunks), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_multi_split(q, k, v, sinks, seqlens_k, num_chunks, scale, partial_o=None, partial_m=None,
+                       partial_d=None):
+    """``sinkattn_decode_multi_split``: q [B, T, Hq, D]; returns (partial_o [B*T, Hq, C, D],
+    partial_m [B*T, Hq, C], partial_d [B*T, Hq, C])."""
+    batch, q_len, hq, dim = q.shape
+    rows = batch * q_len
+    if partial_o is None:
+        partial_o = torch.empty((rows, hq, num_chunks, dim), dtype=torch.float32, device=q.device)
+    if partial_m is None:
+        partial_m = torch.empty((rows, hq, num_chunks), dtype=torch.float32, device=q.device)
+    if partial_d is None:
+        partial_d = torch.empty((rows, hq, num_chunks), dtype=torch.float32, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, seqlens_k, partial_o, partial_m, partial_d)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k, partial_o, partial_m, partial_d)]
+    _lib.check(_lib.lib.sinkattn_decode_multi_split(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        int(num_chunks), float(scale), _lib.ref(d[5]), _lib.ref(d[6]), _lib.ref(d[7]),
+        _lib.stream_handle(dev)))
+    return partial_o, partial_m, partial_d
+
+
+def decode_multi(q, k, v, sinks, seqlens_k, num_chunks, scale, return_lse=False):
+    """Multi-token split then merge (partials allocated with torch); out [B, T, Hq, D]."""
+    batch, q_len, hq, dim = q.shape
+    po, pm, pd = decode_multi_split(q, k, v, sinks, seqlens_k, num_chunks, scale)
+    res = decode_merge(po, pm, pd, out_dtype=q.dtype, return_lse=return_lse)
+    if return_lse:
+        out, lse = res
+        return out.view(batch, q_len, hq, dim), lse.view(batch, q_len, hq)
+    return res.view(batch, q_len, hq, dim)
+
+
+def decode_multi_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, out=None, lse=None,
+                       return_lse=False):
+    """``sinkattn_decode_multi``: out [B, T, Hq, D]; ``workspace`` from
+    ``decode_workspace(B * T, Hq, Hkv, num_chunks, device)``."""
+    batch, q_len, hq, dim = q.shape
+    if out is None:
+        out = torch.empty((batch, q_len, hq, dim), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, q_len, hq), dtype=torch.float32, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, seqlens_k, workspace, out, lse)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k, out, lse)]
+    _lib.check(_lib.lib.sinkattn_decode_multi(
         _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
         int(num_chunks), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))

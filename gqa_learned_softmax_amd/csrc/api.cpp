@@ -116,8 +116,9 @@ sinkattn_status check_contiguous(const sinkattn_tensor* t, const char* name) {
 }
 
 // Writes to an output must not collide: sorted by stride, every dimension must step past the
-// whole extent of the smaller ones.
+// whole extent of the smaller ones. A tensor without elements has nothing to collide.
 sinkattn_status check_no_self_overlap(const sinkattn_tensor* t, const char* name) {
+    if (numel(t) == 0) return SINKATTN_OK;
     int idx[4];
     int n = 0;
     for (int i = 0; i < t->ndim; ++i)
@@ -187,13 +188,16 @@ sinkattn_status launched(hipError_t err) {
     return SINKATTN_OK;
 }
 
-// Validation shared by sinkattn_decode_split and sinkattn_decode: the inputs, chunking and scale.
-// Fills the input half of `p`.
+// Largest G x T query rows per KV head the multi-token decode kernel takes (four 16-column tiles).
+constexpr int64_t kMaxDecodeRows = 64;
+
+// Validation shared by the decode calls: the inputs, chunking and scale. q is [B, Hq, D], or
+// [B, T, Hq, D] when `multi`. Fills the input half of `p`.
 sinkattn_status check_decode_inputs(const sinkattn_tensor* q, const sinkattn_tensor* k,
                                     const sinkattn_tensor* v, const sinkattn_tensor* sinks,
                                     const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
-                                    sinkattn::DecodeSplitParams& p) {
-    SA_TRY(check_desc(q, "q", 3));
+                                    bool multi, sinkattn::DecodeSplitParams& p) {
+    SA_TRY(check_desc(q, "q", multi ? 4 : 3));
     SA_TRY(check_desc(k, "k", 4));
     SA_TRY(check_desc(v, "v", 4));
     if (q->dtype != SINKATTN_BF16 && q->dtype != SINKATTN_F32)
@@ -201,7 +205,9 @@ sinkattn_status check_decode_inputs(const sinkattn_tensor* q, const sinkattn_ten
     SA_TRY(check_dtype(k, "k", q->dtype));
     SA_TRY(check_dtype(v, "v", q->dtype));
 
-    const int64_t batch = q->shape[0], hq = q->shape[1], dim = q->shape[2];
+    const int qo = multi ? 1 : 0;  // q's head axis is qo + 1
+    const int64_t batch = q->shape[0], q_len = multi ? q->shape[1] : 1;
+    const int64_t hq = q->shape[qo + 1], dim = q->shape[qo + 2];
     const int64_t cap = k->shape[1], hkv = k->shape[2];
     for (int i = 0; i < 4; ++i)
         if (v->shape[i] != k->shape[i])
@@ -221,7 +227,12 @@ sinkattn_status check_decode_inputs(const sinkattn_tensor* q, const sinkattn_ten
     if (!is_pow2(group) || group > 16)
         return fail(SINKATTN_ERR_UNSUPPORTED, "group size %lld not supported (1, 2, 4, 8 or 16)",
                     (long long)group);
-    if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
+    if (group * q_len > kMaxDecodeRows)
+        return fail(SINKATTN_ERR_UNSUPPORTED,
+                    "group size x tokens per sequence = %lld exceeds %lld query rows per KV head",
+                    (long long)(group * q_len), (long long)kMaxDecodeRows);
+    if (batch * hkv * num_chunks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31) ||
+        batch * q_len * hq * num_chunks >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
     // Cache rows of one (sequence, KV head) slice are addressed with 32-bit byte offsets,
     // including prefetches up to 512 rows past a chunk end.
@@ -241,7 +252,8 @@ sinkattn_status check_decode_inputs(const sinkattn_tensor* q, const sinkattn_ten
     p.sinks = static_cast<const float*>(sinks->data);
     p.seqlens_k = static_cast<const int32_t*>(seqlens_k->data);
     p.q_stride_b = q->stride[0];
-    p.q_stride_head = q->stride[1];
+    p.q_stride_tok = multi ? q->stride[1] : 0;
+    p.q_stride_head = q->stride[qo + 1];
     p.k_stride_b = k->stride[0];
     p.k_stride_tok = k->stride[1];
     p.k_stride_head = k->stride[2];
@@ -254,6 +266,7 @@ sinkattn_status check_decode_inputs(const sinkattn_tensor* q, const sinkattn_ten
     p.num_q_heads = static_cast<int32_t>(hq);
     p.num_kv_heads = static_cast<int32_t>(hkv);
     p.num_chunks = num_chunks;
+    p.q_len = static_cast<int32_t>(q_len);
     p.scale = scale;
     return SINKATTN_OK;
 }
@@ -349,6 +362,160 @@ sinkattn_status check_prefill_inputs(const sinkattn_tensor* q, const sinkattn_te
     p.causal = causal ? 1 : 0;
     p.num_splits = 1;
     return SINKATTN_OK;
+}
+
+// sinkattn_decode_split (q [B, Hq, D]) and sinkattn_decode_multi_split (q [B, T, Hq, D]); the
+// partials of row (b, t, h) sit at (b * T + t, h), so T = 1 is the single-token layout.
+sinkattn_status decode_split_impl(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                  const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                  const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                  const sinkattn_tensor* partial_o,
+                                  const sinkattn_tensor* partial_m,
+                                  const sinkattn_tensor* partial_d, void* stream, bool multi) {
+    g_last_error.clear();
+    SA_TRY(check_desc(q, "q", multi ? 4 : 3));
+    SA_TRY(check_desc(partial_o, "partial_o", 4));
+    SA_TRY(check_desc(partial_m, "partial_m", 3));
+    SA_TRY(check_desc(partial_d, "partial_d", 3));
+    sinkattn::DecodeSplitParams p{};
+    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, multi, p));
+    SA_TRY(check_dtype(partial_o, "partial_o", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_m, "partial_m", SINKATTN_F32));
+    SA_TRY(check_dtype(partial_d, "partial_d", SINKATTN_F32));
+    const int64_t want_o[4] = {static_cast<int64_t>(p.batch) * p.q_len, p.num_q_heads, num_chunks,
+                               sinkattn::kHeadDim};
+    for (int i = 0; i < 4; ++i)
+        if (partial_o->shape[i] != want_o[i])
+            return fail(SINKATTN_ERR_SHAPE, multi ? "partial_o: expected [B*T, Hq, num_chunks, D]"
+                                                  : "partial_o: expected [B, Hq, num_chunks, D]");
+    for (int i = 0; i < 3; ++i)
+        if (partial_m->shape[i] != want_o[i] || partial_d->shape[i] != want_o[i])
+            return fail(SINKATTN_ERR_SHAPE, multi ? "partial_m/partial_d: expected [B*T, Hq, num_chunks]"
+                                                  : "partial_m/partial_d: expected [B, Hq, num_chunks]");
+    SA_TRY(check_data(partial_o, "partial_o"));
+    SA_TRY(check_data(partial_m, "partial_m"));
+    SA_TRY(check_data(partial_d, "partial_d"));
+    SA_TRY(check_contiguous(partial_o, "partial_o"));
+    SA_TRY(check_contiguous(partial_m, "partial_m"));
+    SA_TRY(check_contiguous(partial_d, "partial_d"));
+    const sinkattn_tensor* outs[3] = {partial_o, partial_m, partial_d};
+    const char* onames[3] = {"partial_o", "partial_m", "partial_d"};
+    const sinkattn_tensor* ins[5] = {q, k, v, sinks, seqlens_k};
+    const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 5; ++b) SA_TRY(check_disjoint(outs[a], onames[a], ins[b], inames[b]));
+        for (int b = a + 1; b < 3; ++b) SA_TRY(check_disjoint(outs[a], onames[a], outs[b], onames[b]));
+    }
+
+    if (p.batch == 0 || p.q_len == 0) return SINKATTN_OK;
+    p.partial_o = static_cast<float*>(partial_o->data);
+    p.partial_m = static_cast<float*>(partial_m->data);
+    p.partial_d = static_cast<float*>(partial_d->data);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_decode_split_bf16(p, s)
+                                              : sinkattn::launch_decode_split_f32(p, s));
+}
+
+// sinkattn_decode (q, out [B, Hq, D], lse [B, Hq]) and sinkattn_decode_multi (q, out [B, T, Hq, D],
+// lse [B, T, Hq]); the workspace holds the partials of B x T rows.
+sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                  const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                  const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                  void* workspace, size_t workspace_bytes,
+                                  const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                  void* stream, bool multi) {
+    g_last_error.clear();
+    const int rank = multi ? 4 : 3;
+    SA_TRY(check_desc(q, "q", rank));
+    SA_TRY(check_desc(out, "out", rank));
+    if (lse != nullptr) SA_TRY(check_desc(lse, "lse", rank - 1));
+    sinkattn::DecodeSplitParams p{};
+    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, multi, p));
+    if (q->dtype == SINKATTN_F32) SA_TRY(check_dtype(out, "out", SINKATTN_F32));
+    else if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
+    if (lse != nullptr) SA_TRY(check_dtype(lse, "lse", SINKATTN_F32));
+    for (int i = 0; i < rank; ++i)
+        if (out->shape[i] != q->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, multi ? "out: expected [B, T, Hq, D]" : "out: expected [B, Hq, D]");
+    for (int i = 0; lse != nullptr && i < rank - 1; ++i)
+        if (lse->shape[i] != q->shape[i])
+            return fail(SINKATTN_ERR_SHAPE, multi ? "lse: expected [B, T, Hq]" : "lse: expected [B, Hq]");
+    const WorkspaceLayout w =
+        workspace_layout(static_cast<int64_t>(p.batch) * p.q_len, p.num_q_heads, p.num_kv_heads, num_chunks);
+    if (workspace_bytes < w.total)
+        return fail(SINKATTN_ERR_SHAPE, "workspace: %zu bytes, need %zu", workspace_bytes, w.total);
+    if (w.total > 0 && workspace == nullptr) return fail(SINKATTN_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(SINKATTN_ERR_LAYOUT, "workspace not 256-byte aligned");
+    SA_TRY(check_data(out, "out"));
+    SA_TRY(check_rows(out, "out"));
+    SA_TRY(check_no_self_overlap(out, "out"));
+    if (lse != nullptr) {
+        SA_TRY(check_data(lse, "lse"));
+        if (reinterpret_cast<uintptr_t>(lse->data) % 4 != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "lse: data pointer not 4-byte aligned");
+        if (lse->stride[rank - 2] != 1 && lse->shape[rank - 2] > 1)
+            return fail(SINKATTN_ERR_LAYOUT, "lse: innermost stride must be 1");
+        SA_TRY(check_no_self_overlap(lse, "lse"));
+    }
+    // The workspace is written too: it may not overlap any tensor argument.
+    sinkattn_tensor ws{};
+    ws.data = workspace;
+    ws.dtype = SINKATTN_F32;
+    ws.ndim = 1;
+    ws.shape[0] = static_cast<int64_t>(w.total / 4);
+    ws.stride[0] = 1;
+    const sinkattn_tensor* ins[5] = {q, k, v, sinks, seqlens_k};
+    const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
+    for (int b = 0; b < 5; ++b) {
+        SA_TRY(check_disjoint(out, "out", ins[b], inames[b]));
+        SA_TRY(check_disjoint(&ws, "workspace", ins[b], inames[b]));
+        if (lse != nullptr) SA_TRY(check_disjoint(lse, "lse", ins[b], inames[b]));
+    }
+    SA_TRY(check_disjoint(out, "out", &ws, "workspace"));
+    if (lse != nullptr) {
+        SA_TRY(check_disjoint(lse, "lse", &ws, "workspace"));
+        SA_TRY(check_disjoint(out, "out", lse, "lse"));
+    }
+
+    if (p.batch == 0 || p.q_len == 0) return SINKATTN_OK;
+    char* base = static_cast<char*>(workspace);
+    p.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+    p.partial_o = reinterpret_cast<float*>(base + w.partial_o);
+    p.partial_m = reinterpret_cast<float*>(base + w.partial_m);
+    p.partial_d = reinterpret_cast<float*>(base + w.partial_d);
+    p.out = out->data;
+    p.lse = lse != nullptr ? static_cast<float*>(lse->data) : nullptr;
+    p.o_stride_b = out->stride[0];
+    p.o_stride_tok = multi ? out->stride[1] : 0;
+    p.o_stride_head = out->stride[rank - 2];
+    p.lse_stride_b = lse != nullptr ? lse->stride[0] : 0;
+    p.lse_stride_tok = lse != nullptr && multi ? lse->stride[1] : 0;
+    p.lse_stride_head = lse != nullptr ? lse->stride[rank - 2] : 0;
+    p.out_is_bf16 = out->dtype == SINKATTN_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (q->dtype == SINKATTN_BF16) return launched(sinkattn::launch_decode_fused_bf16(p, s));
+    // fp32 reference variant: the two-kernel path through the same workspace.
+    SA_TRY(launched(sinkattn::launch_decode_split_f32(p, s)));
+    sinkattn::DecodeMergeParams mp{};
+    mp.partial_o = p.partial_o;
+    mp.partial_m = p.partial_m;
+    mp.partial_d = p.partial_d;
+    mp.out = p.out;
+    mp.lse = p.lse;
+    mp.o_stride_b = p.o_stride_b;
+    mp.o_stride_tok = p.o_stride_tok;
+    mp.o_stride_head = p.o_stride_head;
+    mp.lse_stride_b = p.lse_stride_b;
+    mp.lse_stride_tok = p.lse_stride_tok;
+    mp.lse_stride_head = p.lse_stride_head;
+    mp.batch = p.batch * p.q_len;
+    mp.q_len = p.q_len;
+    mp.num_q_heads = p.num_q_heads;
+    mp.num_chunks = num_chunks;
+    mp.out_is_bf16 = p.out_is_bf16;
+    return launched(sinkattn::launch_decode_merge(mp, s));
 }
 
 }  // namespace
@@ -449,45 +616,18 @@ sinkattn_status sinkattn_decode_split(const sinkattn_tensor* q, const sinkattn_t
                                       float scale, const sinkattn_tensor* partial_o,
                                       const sinkattn_tensor* partial_m,
                                       const sinkattn_tensor* partial_d, void* stream) {
-    g_last_error.clear();
-    SA_TRY(check_desc(q, "q", 3));
-    SA_TRY(check_desc(partial_o, "partial_o", 4));
-    SA_TRY(check_desc(partial_m, "partial_m", 3));
-    SA_TRY(check_desc(partial_d, "partial_d", 3));
-    sinkattn::DecodeSplitParams p{};
-    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, p));
-    SA_TRY(check_dtype(partial_o, "partial_o", SINKATTN_F32));
-    SA_TRY(check_dtype(partial_m, "partial_m", SINKATTN_F32));
-    SA_TRY(check_dtype(partial_d, "partial_d", SINKATTN_F32));
-    const int64_t want_o[4] = {q->shape[0], q->shape[1], num_chunks, q->shape[2]};
-    for (int i = 0; i < 4; ++i)
-        if (partial_o->shape[i] != want_o[i])
-            return fail(SINKATTN_ERR_SHAPE, "partial_o: expected [B, Hq, num_chunks, D]");
-    for (int i = 0; i < 3; ++i)
-        if (partial_m->shape[i] != want_o[i] || partial_d->shape[i] != want_o[i])
-            return fail(SINKATTN_ERR_SHAPE, "partial_m/partial_d: expected [B, Hq, num_chunks]");
-    SA_TRY(check_data(partial_o, "partial_o"));
-    SA_TRY(check_data(partial_m, "partial_m"));
-    SA_TRY(check_data(partial_d, "partial_d"));
-    SA_TRY(check_contiguous(partial_o, "partial_o"));
-    SA_TRY(check_contiguous(partial_m, "partial_m"));
-    SA_TRY(check_contiguous(partial_d, "partial_d"));
-    const sinkattn_tensor* outs[3] = {partial_o, partial_m, partial_d};
-    const char* onames[3] = {"partial_o", "partial_m", "partial_d"};
-    const sinkattn_tensor* ins[5] = {q, k, v, sinks, seqlens_k};
-    const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
-    for (int a = 0; a < 3; ++a) {
-        for (int b = 0; b < 5; ++b) SA_TRY(check_disjoint(outs[a], onames[a], ins[b], inames[b]));
-        for (int b = a + 1; b < 3; ++b) SA_TRY(check_disjoint(outs[a], onames[a], outs[b], onames[b]));
-    }
+    return decode_split_impl(q, k, v, sinks, seqlens_k, num_chunks, scale, partial_o, partial_m,
+                             partial_d, stream, false);
+}
 
-    if (p.batch == 0) return SINKATTN_OK;
-    p.partial_o = static_cast<float*>(partial_o->data);
-    p.partial_m = static_cast<float*>(partial_m->data);
-    p.partial_d = static_cast<float*>(partial_d->data);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return launched(q->dtype == SINKATTN_BF16 ? sinkattn::launch_decode_split_bf16(p, s)
-                                              : sinkattn::launch_decode_split_f32(p, s));
+sinkattn_status sinkattn_decode_multi_split(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                            const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                            const sinkattn_tensor* seqlens_k, int num_chunks,
+                                            float scale, const sinkattn_tensor* partial_o,
+                                            const sinkattn_tensor* partial_m,
+                                            const sinkattn_tensor* partial_d, void* stream) {
+    return decode_split_impl(q, k, v, sinks, seqlens_k, num_chunks, scale, partial_o, partial_m,
+                             partial_d, stream, true);
 }
 
 sinkattn_status sinkattn_decode(const sinkattn_tensor* q, const sinkattn_tensor* k,
@@ -496,89 +636,18 @@ sinkattn_status sinkattn_decode(const sinkattn_tensor* q, const sinkattn_tensor*
                                 void* workspace, size_t workspace_bytes,
                                 const sinkattn_tensor* out, const sinkattn_tensor* lse,
                                 void* stream) {
-    g_last_error.clear();
-    SA_TRY(check_desc(q, "q", 3));
-    SA_TRY(check_desc(out, "out", 3));
-    if (lse != nullptr) SA_TRY(check_desc(lse, "lse", 2));
-    sinkattn::DecodeSplitParams p{};
-    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, p));
-    if (q->dtype == SINKATTN_F32) SA_TRY(check_dtype(out, "out", SINKATTN_F32));
-    else if (out->dtype != SINKATTN_BF16 && out->dtype != SINKATTN_F32)
-        return fail(SINKATTN_ERR_DTYPE, "out: dtype must be bf16 or f32");
-    if (lse != nullptr) SA_TRY(check_dtype(lse, "lse", SINKATTN_F32));
-    for (int i = 0; i < 3; ++i)
-        if (out->shape[i] != q->shape[i]) return fail(SINKATTN_ERR_SHAPE, "out: expected [B, Hq, D]");
-    if (lse != nullptr && (lse->shape[0] != q->shape[0] || lse->shape[1] != q->shape[1]))
-        return fail(SINKATTN_ERR_SHAPE, "lse: expected [B, Hq]");
-    const WorkspaceLayout w = workspace_layout(p.batch, p.num_q_heads, p.num_kv_heads, num_chunks);
-    if (workspace_bytes < w.total)
-        return fail(SINKATTN_ERR_SHAPE, "workspace: %zu bytes, need %zu", workspace_bytes, w.total);
-    if (w.total > 0 && workspace == nullptr) return fail(SINKATTN_ERR_NULL, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-        return fail(SINKATTN_ERR_LAYOUT, "workspace not 256-byte aligned");
-    SA_TRY(check_data(out, "out"));
-    SA_TRY(check_rows(out, "out"));
-    SA_TRY(check_no_self_overlap(out, "out"));
-    if (lse != nullptr) {
-        SA_TRY(check_data(lse, "lse"));
-        if (reinterpret_cast<uintptr_t>(lse->data) % 4 != 0)
-            return fail(SINKATTN_ERR_LAYOUT, "lse: data pointer not 4-byte aligned");
-        if (lse->stride[1] != 1 && lse->shape[1] > 1)
-            return fail(SINKATTN_ERR_LAYOUT, "lse: innermost stride must be 1");
-        SA_TRY(check_no_self_overlap(lse, "lse"));
-    }
-    // The workspace is written too: it may not overlap any tensor argument.
-    sinkattn_tensor ws{};
-    ws.data = workspace;
-    ws.dtype = SINKATTN_F32;
-    ws.ndim = 1;
-    ws.shape[0] = static_cast<int64_t>(w.total / 4);
-    ws.stride[0] = 1;
-    const sinkattn_tensor* ins[5] = {q, k, v, sinks, seqlens_k};
-    const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
-    for (int b = 0; b < 5; ++b) {
-        SA_TRY(check_disjoint(out, "out", ins[b], inames[b]));
-        SA_TRY(check_disjoint(&ws, "workspace", ins[b], inames[b]));
-        if (lse != nullptr) SA_TRY(check_disjoint(lse, "lse", ins[b], inames[b]));
-    }
-    SA_TRY(check_disjoint(out, "out", &ws, "workspace"));
-    if (lse != nullptr) {
-        SA_TRY(check_disjoint(lse, "lse", &ws, "workspace"));
-        SA_TRY(check_disjoint(out, "out", lse, "lse"));
-    }
+    return decode_fused_impl(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace,
+                             workspace_bytes, out, lse, stream, false);
+}
 
-    if (p.batch == 0) return SINKATTN_OK;
-    char* base = static_cast<char*>(workspace);
-    p.counters = reinterpret_cast<uint32_t*>(base + w.counters);
-    p.partial_o = reinterpret_cast<float*>(base + w.partial_o);
-    p.partial_m = reinterpret_cast<float*>(base + w.partial_m);
-    p.partial_d = reinterpret_cast<float*>(base + w.partial_d);
-    p.out = out->data;
-    p.lse = lse != nullptr ? static_cast<float*>(lse->data) : nullptr;
-    p.o_stride_b = out->stride[0];
-    p.o_stride_head = out->stride[1];
-    p.lse_stride_b = lse != nullptr ? lse->stride[0] : 0;
-    p.lse_stride_head = lse != nullptr ? lse->stride[1] : 0;
-    p.out_is_bf16 = out->dtype == SINKATTN_BF16;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (q->dtype == SINKATTN_BF16) return launched(sinkattn::launch_decode_fused_bf16(p, s));
-    // fp32 reference variant: the two-kernel path through the same workspace.
-    SA_TRY(launched(sinkattn::launch_decode_split_f32(p, s)));
-    sinkattn::DecodeMergeParams mp{};
-    mp.partial_o = p.partial_o;
-    mp.partial_m = p.partial_m;
-    mp.partial_d = p.partial_d;
-    mp.out = p.out;
-    mp.lse = p.lse;
-    mp.o_stride_b = p.o_stride_b;
-    mp.o_stride_head = p.o_stride_head;
-    mp.lse_stride_b = p.lse_stride_b;
-    mp.lse_stride_head = p.lse_stride_head;
-    mp.batch = p.batch;
-    mp.num_q_heads = p.num_q_heads;
-    mp.num_chunks = num_chunks;
-    mp.out_is_bf16 = p.out_is_bf16;
-    return launched(sinkattn::launch_decode_merge(mp, s));
+sinkattn_status sinkattn_decode_multi(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                      const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                      const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                      void* workspace, size_t workspace_bytes,
+                                      const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                      void* stream) {
+    return decode_fused_impl(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace,
+                             workspace_bytes, out, lse, stream, true);
 }
 
 size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
@@ -665,6 +734,7 @@ sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
     p.lse_stride_b = lse != nullptr ? lse->stride[0] : 0;
     p.lse_stride_head = lse != nullptr ? lse->stride[1] : 0;
     p.batch = static_cast<int32_t>(batch);
+    p.q_len = 1;
     p.num_q_heads = static_cast<int32_t>(hq);
     p.num_chunks = num_chunks;
     p.out_is_bf16 = out->dtype == SINKATTN_BF16;

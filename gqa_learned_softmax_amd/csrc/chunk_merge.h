@@ -68,4 +68,45 @@ __device__ __forceinline__ void merge_chunk_states(const float* pm, const float*
     lse = wsum > 0.0f ? big + logf(wsum) : kNegInf;
 }
 
+// Four rows per wave: the same combination with each 16-lane quarter of the wave on its own row
+// (pm/pd/po of the calling lane's row). Lane j of a quarter loads (m_c, d_c) of chunks c = j,
+// j + 16, ..., and channels 4j .. 4j + 3 of every chunk's o (16-byte loads), so a wave has the
+// loads of four rows in flight at once; weights are broadcast inside the quarter. Rows with many
+// more chunks than 16 are better served by merge_chunk_states.
+__device__ __forceinline__ void merge_chunk_states_x4(const float* pm, const float* pd, const float* po,
+                                                      int chunks, int lane, f32x4& out, float& lse) {
+    const int j = lane & 15;
+    const int quarter = lane & 48;
+    float big = kNegInf;
+    for (int c = j; c - j < chunks; c += 16) big = fmaxf(big, c < chunks ? pm[c] : kNegInf);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) big = fmaxf(big, __shfl_xor(big, o));
+    float wsum = 0.0f;
+    f32x4 osum = zero_f32x4();
+    if (big != kNegInf) {
+        for (int c0 = 0; c0 < chunks; c0 += 16) {
+            const int c = c0 + j;
+            const float mc = c < chunks ? pm[c] : kNegInf;
+            const float w = mc == kNegInf ? 0.0f : pd[c] * expf(mc - big);
+            wsum += w;
+            const int n = chunks - c0 < 16 ? chunks - c0 : 16;
+            const float* rows = po + static_cast<int64_t>(c0) * kHeadDim + 4 * j;
+            int u = 0;
+            for (; u + 4 <= n; u += 4) {
+                f32x4 o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = *reinterpret_cast<const f32x4*>(rows + (u + e) * kHeadDim);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) osum += __shfl(w, quarter + u + e) * o[e];
+            }
+            for (; u < n; ++u)
+                osum += __shfl(w, quarter + u) * *reinterpret_cast<const f32x4*>(rows + u * kHeadDim);
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+    }
+    out = wsum > 0.0f ? osum / wsum : zero_f32x4();
+    lse = wsum > 0.0f ? big + logf(wsum) : kNegInf;
+}
+
 }  // namespace sinkattn

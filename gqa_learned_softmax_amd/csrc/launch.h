@@ -39,7 +39,8 @@ struct PrefillParams {
     float* partial_d;
 };
 
-// Split-KV decode. q [B, Hq, D]; k/v [B, Lcap, Hkv, D]; partials contiguous.
+// Split-KV decode of q_len tokens per sequence. q [B, T, Hq, D] (T = 1: [B, Hq, D]);
+// k/v [B, Lcap, Hkv, D]; partials contiguous [B, T, Hq, C, D] / [B, T, Hq, C].
 struct DecodeSplitParams {
     const void* q;
     const void* k;
@@ -49,7 +50,7 @@ struct DecodeSplitParams {
     float* partial_o;
     float* partial_m;
     float* partial_d;
-    int64_t q_stride_b, q_stride_head;
+    int64_t q_stride_b, q_stride_tok, q_stride_head;
     int64_t k_stride_b, k_stride_tok, k_stride_head;
     int64_t v_stride_b, v_stride_tok, v_stride_head;
     int64_t capacity;    // Lcap
@@ -58,26 +59,30 @@ struct DecodeSplitParams {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t num_chunks;
+    int32_t q_len;       // T >= 1 tokens per sequence, the last T of its seqlens_k keys
     float scale;
     // Fused split + merge only (sinkattn_decode): zero-initialised completion counters, one per
     // (sequence, KV head), and the merged outputs.
     uint32_t* counters;
     void* out;
     float* lse;          // may be null
-    int64_t o_stride_b, o_stride_head;
-    int64_t lse_stride_b, lse_stride_head;
+    int64_t o_stride_b, o_stride_tok, o_stride_head;
+    int64_t lse_stride_b, lse_stride_tok, lse_stride_head;
     int32_t out_is_bf16;
 };
 
+// Merge of rows (b, t, h): partials contiguous [batch, Hq, C, D] with batch = B x q_len; the
+// output of row (b, t, h) sits at b * o_stride_b + t * o_stride_tok + h * o_stride_head.
 struct DecodeMergeParams {
     const float* partial_o;
     const float* partial_m;
     const float* partial_d;
     void* out;
     float* lse;          // may be null
-    int64_t o_stride_b, o_stride_head;
-    int64_t lse_stride_b, lse_stride_head;
+    int64_t o_stride_b, o_stride_tok, o_stride_head;
+    int64_t lse_stride_b, lse_stride_tok, lse_stride_head;
     int32_t batch;
+    int32_t q_len;
     int32_t num_q_heads;
     int32_t num_chunks;
     int32_t out_is_bf16;

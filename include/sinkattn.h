@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_VERSION 3
+#define SINKATTN_VERSION 4
 
 typedef enum {
     SINKATTN_OK = 0,
@@ -222,6 +222,51 @@ sinkattn_status sinkattn_decode(const sinkattn_tensor* q, const sinkattn_tensor*
                                 const sinkattn_tensor* out, const sinkattn_tensor* lse,
                                 void* stream);
 
+/*
+ * sinkattn_decode_multi_split - T new tokens per sequence (speculative or multi-token
+ * verification) against the padded KV cache that already holds them, split along the KV length.
+ *
+ * Source: "GPT-OSS on Day 0", "Sink attention" subsection, as for sinkattn_decode_split (heads and
+ * KV length in parallel, sink in the first chunk only), for the T last rows of a causal sequence:
+ * with L = seqlens_k[b] keys (the T new tokens included), token t of sequence b sees keys
+ * j <= L - T + t (the causal rule of sinkattn_prefill for Lq = T, Lk = L). The G = Hq/Hkv heads
+ * and T tokens that share a KV head are computed together, so the cache is read once for all of
+ * them.
+ *
+ *   q          [B, T, Hq, D]       bf16 | fp32
+ *   k, v, sinks, seqlens_k, num_chunks, scale: as for sinkattn_decode_split (chunk c covers keys
+ *              [c*cs, (c+1)*cs), cs = ceil(Lcap / num_chunks), each token clipped to its own limit;
+ *              chunk 0 always carries the sink)
+ *   partial_o  [B*T, Hq, C, D] fp32, contiguous  (row b*T + t holds token t of sequence b)
+ *   partial_m, partial_d [B*T, Hq, C] fp32, contiguous
+ * The states follow sinkattn_decode_split's definition per (b, t, h, c); sinkattn_decode_merge on
+ * these partials with out viewed as [B*T, Hq, D] gives the attention outputs. Supported: group
+ * sizes 1, 2, 4, 8, 16 with G * T <= 64. B = 0 or T = 0 launches nothing.
+ */
+sinkattn_status sinkattn_decode_multi_split(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                            const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                            const sinkattn_tensor* seqlens_k, int num_chunks,
+                                            float scale, const sinkattn_tensor* partial_o,
+                                            const sinkattn_tensor* partial_m,
+                                            const sinkattn_tensor* partial_d, void* stream);
+/*
+ * sinkattn_decode_multi - sinkattn_decode_multi_split and the merge in one launch, as
+ * sinkattn_decode does for one token.
+ *
+ *   q               [B, T, Hq, D] bf16 | fp32
+ *   workspace       as for sinkattn_decode, sized by sinkattn_decode_workspace_size(B * T, Hq, Hkv,
+ *                   num_chunks), with its first sinkattn_decode_workspace_counter_bytes(B * T, Hkv)
+ *                   bytes zero before the first call (left zero by every completed call)
+ *   out             [B, T, Hq, D] bf16 | fp32 (fp32 only if q is fp32)
+ *   lse             [B, T, Hq] fp32 or NULL
+ * Other arguments and limits as for sinkattn_decode_multi_split.
+ */
+sinkattn_status sinkattn_decode_multi(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                      const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                      const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                      void* workspace, size_t workspace_bytes,
+                                      const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                      void* stream);
 /* Bytes of workspace sinkattn_decode needs (0 for invalid arguments). */
 size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
                                       int num_chunks);

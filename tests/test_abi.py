@@ -339,3 +339,91 @@ def test_fused_rejects(name, mutate, code):
     status = call_fused(mutate(fused_args()))
     assert status == code, (status, last_error())
     assert last_error()
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+def msplit_args(b=2, t=3, hq=8, hkv=1, cap=64, chunks=4, dim=64, dtype=BF16):
+    return dict(q=T([b, t, hq, dim], dtype), k=T([b, cap, hkv, dim], dtype), v=T([b, cap, hkv, dim], dtype),
+                sinks=T([hq], F32), seqlens=T([b], I32), chunks=chunks, scale=0.125,
+                po=T([b * t, hq, chunks, dim], F32), pm=T([b * t, hq, chunks], F32),
+                pd=T([b * t, hq, chunks], F32))
+
+
+def call_msplit(a):
+    return _lib.lib.sinkattn_decode_multi_split(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]),
+                                                R(a["seqlens"]), a["chunks"], a["scale"], R(a["po"]),
+                                                R(a["pm"]), R(a["pd"]), None)
+
+
+@pytest.mark.parametrize("b,t", [(0, 3), (2, 0)])
+def test_multi_split_empty_is_ok(b, t):
+    assert call_msplit(msplit_args(b=b, t=t)) == _lib.OK
+
+
+MSPLIT_CASES = [
+    ("q_rank3", lambda a: _mut(a, q=T([2, 8, 64])), _lib.ERR_SHAPE),
+    ("partial_rows_b_not_bt", lambda a: _mut(a, po=T([2, 8, 4, 64], F32)), _lib.ERR_SHAPE),
+    ("pm_rows_b_not_bt", lambda a: _mut(a, pm=T([2, 8, 4], F32)), _lib.ERR_SHAPE),
+    ("k_batch", lambda a: _mut(a, k=T([3, 64, 1, 64]), v=T([3, 64, 1, 64])), _lib.ERR_SHAPE),
+    ("sinks_len", lambda a: _mut(a, sinks=T([4], F32)), _lib.ERR_SHAPE),
+    ("chunks_zero", lambda a: _mut(a, chunks=0), _lib.ERR_SHAPE),
+    ("rows_over_64", lambda a: msplit_args(t=9), _lib.ERR_UNSUPPORTED),
+    ("group16_t5", lambda a: msplit_args(hq=16, t=5), _lib.ERR_UNSUPPORTED),
+    ("group_6", lambda a: msplit_args(hq=6), _lib.ERR_UNSUPPORTED),
+    ("q_f32_k_bf16", lambda a: _mut(a, q=T([2, 3, 8, 64], F32)), _lib.ERR_DTYPE),
+    ("q_token_stride_odd", lambda a: _mut(a, q=T([2, 3, 8, 64], strides=[1544, 515, 64, 1])), _lib.ERR_LAYOUT),
+    ("partial_overlaps_q", lambda a: _mut(a, po=T([6, 8, 4, 64], F32, addr=a["q"].data)), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", MSPLIT_CASES, ids=[c[0] for c in MSPLIT_CASES])
+def test_multi_split_rejects(name, mutate, code):
+    status = call_msplit(mutate(msplit_args()))
+    assert status == code, (status, last_error())
+    assert last_error()
+
+
+def test_multi_split_accepts_the_largest_row_count():
+    # G x T = 64 rows (8 x 8 and 16 x 4) pass validation; the B = 0 batch launches nothing.
+    assert call_msplit(msplit_args(b=0, t=8, hq=8)) == _lib.OK
+    assert call_msplit(msplit_args(b=0, t=4, hq=16)) == _lib.OK
+
+
+def mfused_args(b=2, t=3, hq=8, hkv=1, cap=64, chunks=4, dim=64, dtype=BF16, lse=True):
+    a = dict(q=T([b, t, hq, dim], dtype), k=T([b, cap, hkv, dim], dtype), v=T([b, cap, hkv, dim], dtype),
+             sinks=T([hq], F32), seqlens=T([b], I32), chunks=chunks, scale=0.125,
+             out=T([b, t, hq, dim], dtype), lse=T([b, t, hq], F32) if lse else None)
+    a["ws_bytes"] = _lib.lib.sinkattn_decode_workspace_size(b * t, hq, hkv, chunks)
+    a["ws"] = T([max(1, a["ws_bytes"] // 4)], F32).data
+    return a
+
+
+def call_mfused(a):
+    return _lib.lib.sinkattn_decode_multi(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]), R(a["seqlens"]),
+                                          a["chunks"], a["scale"], a["ws"], a["ws_bytes"], R(a["out"]),
+                                          R(a["lse"]), None)
+
+
+def test_multi_fused_empty_is_ok():
+    assert call_mfused(mfused_args(b=0)) == _lib.OK
+    assert call_mfused(mfused_args(t=0)) == _lib.OK
+
+
+MFUSED_CASES = [
+    ("ws_sized_for_b_not_bt", lambda a: _mut(a, ws_bytes=_lib.lib.sinkattn_decode_workspace_size(2, 8, 1, 4)),
+     _lib.ERR_SHAPE),
+    ("out_rank3", lambda a: _mut(a, out=T([6, 8, 64])), _lib.ERR_SHAPE),
+    ("out_tokens", lambda a: _mut(a, out=T([2, 2, 8, 64])), _lib.ERR_SHAPE),
+    ("lse_rank2", lambda a: _mut(a, lse=T([6, 8], F32)), _lib.ERR_SHAPE),
+    ("lse_tokens", lambda a: _mut(a, lse=T([2, 4, 8], F32)), _lib.ERR_SHAPE),
+    ("lse_inner_stride", lambda a: _mut(a, lse=T([2, 3, 8], F32, strides=[48, 16, 2])), _lib.ERR_LAYOUT),
+    ("rows_over_64", lambda a: mfused_args(t=9), _lib.ERR_UNSUPPORTED),
+    ("ws_overlaps_q", lambda a: _mut(a, ws=a["q"].data), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", MFUSED_CASES, ids=[c[0] for c in MFUSED_CASES])
+def test_multi_fused_rejects(name, mutate, code):
+    status = call_mfused(mutate(mfused_args()))
+    assert status == code, (status, last_error())
+    assert last_error()

@@ -562,3 +562,149 @@ def test_graph_replays_fused_decode():
         sa.decode_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+def oracle_decode_multi(case):
+    """Oracle multi-token decode, one sequence at a time."""
+    outs, lses = [], []
+    for b in range(case.q.shape[0]):
+        n = int(case.seqlens_k[b])
+        o, l = oracle.decode_multi(_np(case.q[b:b + 1]), _np32(case.k[b:b + 1, :n]), _np32(case.v[b:b + 1, :n]),
+                                   _np(case.sinks), [n], case.scale)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def check_multi_partials(po, pm, pd, case, checker, label):
+    """Chunk-level parity per (b, t, h, c): o_c and the chunk log-mass m_c + ln d_c."""
+    ro, rm, rd = oracle.decode_multi_split(_np(case.q), _np32(case.k), _np32(case.v), _np(case.sinks),
+                                           case.seqlens_k.numpy(), case.num_chunks, case.scale)
+    checker(po, ro, f"{label} partial_o")
+    gm, gd = _np(pm), _np(pd)
+    with np.errstate(divide="ignore"):
+        g_mass = np.where(gd > 0, gm + np.log(np.where(gd > 0, gd, 1.0)), -np.inf)
+        r_mass = np.where(rd > 0, rm + np.log(np.where(rd > 0, rd, 1.0)), -np.inf)
+    assert np.array_equal(np.isneginf(g_mass), np.isneginf(r_mass)), f"{label}: empty-chunk pattern"
+    fin = np.isfinite(r_mass)
+    np.testing.assert_allclose(g_mass[fin], r_mass[fin], rtol=0, atol=1e-3 if checker is check_bf16 else 1e-5)
+    assert np.all(gd[~fin] == 0) and np.all(_np(po)[~fin] == 0)
+
+
+MULTI_CASES = [
+    # (name, lens, cap, chunks, Hq, Hkv, T): G x T query rows per KV head in 16-column tiles
+    ("t2_uniform", [512, 512], 512, 4, 64, 8, 2),                     # 16 rows, one tile
+    ("t3_partial_tile", [300, 77, 5], 320, 4, 64, 8, 3),              # 24 rows, two tiles
+    ("t4_ragged_short", [1, 0, 33, 700, 1023, 64], 1024, 8, 64, 8, 4),  # lengths below T
+    ("t5_three_tiles", [450, 129], 512, 4, 64, 8, 5),                 # 40 rows
+    ("t7_four_tiles", [260, 64, 3], 320, 5, 64, 8, 7),                # 56 rows
+    ("t8_four_tiles", [1000, 517, 8, 9], 1024, 8, 64, 8, 8),          # 64 rows
+    ("t8_mask_straddles_chunk", [130, 131], 192, 3, 64, 8, 8),        # masked keys on both sides of 128
+    ("t8_many_chunks", [257, 100], 257, 40, 64, 8, 8),
+    ("t2_group16", [333, 40], 400, 5, 64, 4, 2),                      # 32 rows
+    ("t4_group16", [333, 40], 400, 5, 64, 4, 4),                      # 64 rows
+    ("t8_group1", [200, 31], 256, 4, 8, 8, 8),                        # 8 rows
+    ("t6_group2", [150, 6], 160, 3, 16, 8, 6),                        # 12 rows
+    ("t3_odd_kv_heads", [300, 77], 320, 4, 12, 3, 3),
+    ("t2_paired_heads", [250, 3, 0, 129], 256, 16, 64, 8, 2),         # paired-head work-groups
+    ("t4_paired_heads", [250, 3, 0, 129], 256, 16, 64, 8, 4),
+    ("t1_is_decode", [700, 5], 768, 4, 64, 8, 1),
+]
+
+
+@pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,t", MULTI_CASES, ids=[c[0] for c in MULTI_CASES])
+def test_decode_multi_bf16(name, lens, cap, chunks, hq, hkv, t):
+    sa = _sa()
+    case = workloads.make_decode(lens, cap, chunks, num_q_heads=hq, num_kv_heads=hkv, seed=_seed(name),
+                                 poison=True, q_len=t)
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    po, pm, pd = sa.decode_multi_split(q, k, v, sinks, sl, chunks, case.scale)
+    out, lse = sa.decode_merge(po, pm, pd, out_dtype=q.dtype, return_lse=True)
+    torch.cuda.synchronize()
+    check_multi_partials(po, pm, pd, case, check_bf16, f"multi {name}")
+    ref, rlse = oracle_decode_multi(case)
+    b = len(lens)
+    check_bf16(out.view(b, t, hq, 64), ref, f"multi {name}")
+    g = _np(lse).reshape(rlse.shape)
+    assert np.array_equal(np.isneginf(g), np.isneginf(rlse))
+    fin = np.isfinite(rlse)
+    np.testing.assert_allclose(g[fin], rlse[fin], rtol=0, atol=1e-3)
+    if t == 1:  # the single-token entry point computes the same partials
+        so, sm, sd = sa.decode_split(q[:, 0], k, v, sinks, sl, chunks, case.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(so, po) and torch.equal(sm, pm) and torch.equal(sd, pd)
+
+
+@pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,t",
+                         [c for c in MULTI_CASES if c[0] in ("t3_partial_tile", "t4_ragged_short", "t8_four_tiles",
+                                                             "t4_paired_heads", "t6_group2")],
+                         ids=lambda x: x if isinstance(x, str) else None)
+def test_decode_multi_fused_bf16(name, lens, cap, chunks, hq, hkv, t):
+    sa = _sa()
+    case = workloads.make_decode(lens, cap, chunks, num_q_heads=hq, num_kv_heads=hkv, seed=_seed(name),
+                                 poison=True, q_len=t)
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    b = len(lens)
+    ws = sa.decode_workspace(b * t, hq, hkv, chunks, "cuda")
+    ref, rlse = oracle_decode_multi(case)
+    for call in range(2):  # the second call reuses the workspace the first left behind
+        out, lse = sa.decode_multi_fused(q, k, v, sinks, sl, chunks, case.scale, ws, return_lse=True)
+        torch.cuda.synchronize()
+        check_bf16(out, ref, f"multi fused {name} call {call}")
+        g = _np(lse)
+        assert np.array_equal(np.isneginf(g), np.isneginf(rlse))
+        fin = np.isfinite(rlse)
+        np.testing.assert_allclose(g[fin], rlse[fin], atol=1e-3)
+    counter_bytes = sa._lib.lib.sinkattn_decode_workspace_counter_bytes(b * t, hkv)
+    assert torch.count_nonzero(ws[:counter_bytes]).item() == 0, "counters not reset"
+
+
+def test_decode_multi_strided_query_and_output_views():
+    """q and out as views with padded token and head strides."""
+    sa = _sa()
+    case = workloads.make_decode([400, 90], 512, 4, seed=811, poison=True, q_len=4)
+    q_buf = torch.zeros((2, 4, 64, 128), dtype=torch.bfloat16)
+    q_buf[..., :64] = case.q
+    q_view = q_buf.cuda()[..., :64]
+    k, v, sinks, sl = _dev(case.k, case.v, case.sinks, case.seqlens_k)
+    ws = sa.decode_workspace(8, 64, 8, 4, "cuda")
+    out_buf = torch.zeros((2, 5, 64, 64), dtype=torch.bfloat16, device="cuda")
+    out_view = out_buf[:, 1:]
+    sa.decode_multi_fused(q_view, k, v, sinks, sl, 4, case.scale, ws, out=out_view)
+    po, pm, pd = sa.decode_multi_split(q_view, k, v, sinks, sl, 4, case.scale)
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode_multi(case)
+    check_bf16(out_view, ref, "multi fused strided")
+    check_multi_partials(po, pm, pd, case, check_bf16, "multi split strided")
+    assert torch.all(out_buf[:, 0] == 0), "row outside the view was written"
+
+
+def test_decode_multi_fp32_tiny():
+    sa = _sa()
+    case = workloads.make_decode([37, 2, 0], 48, 3, num_q_heads=8, num_kv_heads=2, dtype=torch.float32,
+                                 seed=821, poison=True, q_len=3)
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    po, pm, pd = sa.decode_multi_split(q, k, v, sinks, sl, 3, case.scale)
+    out = sa.decode_merge(po, pm, pd, out_dtype=torch.float32)
+    ws = sa.decode_workspace(9, 8, 2, 3, "cuda")
+    fused = sa.decode_multi_fused(q, k, v, sinks, sl, 3, case.scale, ws)
+    torch.cuda.synchronize()
+    check_multi_partials(po, pm, pd, case, check_f32, "multi tiny f32")
+    ref, _ = oracle_decode_multi(case)
+    check_f32(out.view(3, 3, 8, 64), ref, "multi tiny f32")
+    check_f32(fused, ref, "multi fused tiny f32")
+
+
+def test_full_multi_decode_8x8192_t4():
+    """The decode workload's shape (8 sequences, 8192-key cache, 64/8 heads) with 4 new tokens each;
+    every output compared."""
+    sa = _sa()
+    lens = [8192] * 8
+    case = workloads.make_decode(lens, 8192, 8, seed=831, q_len=4)
+    q, k, v, sinks, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+    ws = sa.decode_workspace(32, 64, 8, 8, "cuda")
+    out = sa.decode_multi_fused(q, k, v, sinks, sl, 8, case.scale, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle_decode_multi(case)
+    check_bf16(out, ref, "multi full t4")

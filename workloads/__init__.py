@@ -58,9 +58,9 @@ class PrefillCase:
 
 @dataclass
 class DecodeCase:
-    """Single-token decode inputs against a padded KV cache (CPU tensors)."""
+    """Decode inputs against a padded KV cache (CPU tensors): one or q_len new tokens per sequence."""
 
-    q: torch.Tensor          # [B, Hq, D]
+    q: torch.Tensor          # [B, Hq, D], or [B, T, Hq, D] for multi-token decode
     k: torch.Tensor          # [B, Lcap, Hkv, D]
     v: torch.Tensor          # [B, Lcap, Hkv, D]
     sinks: torch.Tensor      # [Hq] float32
@@ -122,8 +122,11 @@ def make_prefill(lens_q, lens_k=None, *, num_q_heads=64, num_kv_heads=8, head_di
 def make_decode(lens, capacity, num_chunks, *, num_q_heads=64, num_kv_heads=8,
                 head_dim=HEAD_DIM, dtype=torch.bfloat16, sink_range=(-2.0, 2.0),
                 sink_normal=False, outlier_p=0.0, outlier_scale=8.0, seed=0, scale=SCALE,
-                poison=False) -> DecodeCase:
+                poison=False, q_len=None) -> DecodeCase:
     """KV cache [B, capacity, Hkv, D]; rows at or past each length are zero, or NaN if ``poison``.
+
+    q is [B, Hq, D], or [B, q_len, Hq, D] for multi-token decode (the lengths then count the
+    q_len new tokens, whose keys are already in the cache).
 
     Only the valid rows are drawn (one sequence at a time, to bound host memory).  With
     ``outlier_p`` > 0 each valid K row (b, t, g) is independently multiplied by ``outlier_scale``
@@ -132,7 +135,8 @@ def make_decode(lens, capacity, num_chunks, *, num_q_heads=64, num_kv_heads=8,
     gen = _gen(seed)
     batch = len(lens)
     fill = float("nan") if poison else 0.0
-    q = _normal((batch, num_q_heads, head_dim), gen, dtype)
+    q_shape = (batch, num_q_heads, head_dim) if q_len is None else (batch, q_len, num_q_heads, head_dim)
+    q = _normal(q_shape, gen, dtype)
     k = torch.full((batch, capacity, num_kv_heads, head_dim), fill, dtype=dtype)
     v = torch.full((batch, capacity, num_kv_heads, head_dim), fill, dtype=dtype)
     for b, n in enumerate(lens):

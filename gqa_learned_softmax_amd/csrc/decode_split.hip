@@ -98,8 +98,8 @@ __device__ __forceinline__ void tile_softmax(const f32x4 (&s)[4], float& m, floa
 // arrive merges all chunks of the set's query rows (set_rows heads x T tokens) and writes out/lse.
 // The barrier orders every wave's stores before thread 0's device-scope release fence (an L2
 // write-back); only the last arrival takes the acquire fence (an L2 and L1 invalidate), after which
-// it reads every chunk's states whichever XCD produced them. One token: one wave per row at a time;
-// several tokens: four rows per wave at a time.
+// it reads every chunk's states whichever XCD produced them. Each wave merges four rows at a time
+// (measured 0.7 us faster than one row per wave on 8 x 8192 keys, one token).
 template <int kWaves>
 __device__ __forceinline__ void fused_merge_tail(const DecodeSplitParams& p, int b, int head_set, int set_rows,
                                                  int heads_per_row, int wave_all, int& last_arrival) {
@@ -115,44 +115,28 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeSplitParams& p, int
     if (!last_arrival) return;
     const int lane = threadIdx.x & 63;
     const int q_len = p.q_len;
-    if (q_len == 1) {
-        for (int hl = wave_all; hl < set_rows; hl += kWaves) {
-            const int h = head_set * set_rows + hl;
-            const int64_t bh = static_cast<int64_t>(b) * p.num_q_heads + h;
-            float o, lse;
-            merge_chunk_states(p.partial_m + bh * p.num_chunks, p.partial_d + bh * p.num_chunks,
-                               p.partial_o + bh * p.num_chunks * kHeadDim, p.num_chunks, lane, o, lse);
-            const int64_t off = b * p.o_stride_b + h * p.o_stride_head + lane;
-            if (p.out_is_bf16)
-                static_cast<__bf16*>(p.out)[off] = (__bf16)o;
-            else
-                static_cast<float*>(p.out)[off] = o;
-            if (p.lse != nullptr && lane == 0) p.lse[b * p.lse_stride_b + h * p.lse_stride_head] = lse;
-        }
-    } else {
-        const int rows = set_rows * q_len;
-        for (int r0 = 4 * wave_all; r0 < rows; r0 += 4 * kWaves) {
-            const int hl = r0 + (lane >> 4);
-            if (hl >= rows) continue;
-            const int tok = hl / set_rows;
-            const int h = head_set * set_rows + hl % set_rows;
-            const int64_t bh = (static_cast<int64_t>(b) * q_len + tok) * p.num_q_heads + h;
-            f32x4 o;
-            float lse;
-            merge_chunk_states_x4(p.partial_m + bh * p.num_chunks, p.partial_d + bh * p.num_chunks,
-                                  p.partial_o + bh * p.num_chunks * kHeadDim, p.num_chunks, lane, o, lse);
-            const int64_t off = b * p.o_stride_b + tok * p.o_stride_tok + h * p.o_stride_head + 4 * (lane & 15);
-            if (p.out_is_bf16) {
-                bf16x4 ob;
+    const int rows = set_rows * q_len;
+    for (int r0 = 4 * wave_all; r0 < rows; r0 += 4 * kWaves) {
+        const int hl = r0 + (lane >> 4);
+        if (hl >= rows) continue;
+        const int tok = hl / set_rows;
+        const int h = head_set * set_rows + hl % set_rows;
+        const int64_t bh = (static_cast<int64_t>(b) * q_len + tok) * p.num_q_heads + h;
+        f32x4 o;
+        float lse;
+        merge_chunk_states_x4(p.partial_m + bh * p.num_chunks, p.partial_d + bh * p.num_chunks,
+                              p.partial_o + bh * p.num_chunks * kHeadDim, p.num_chunks, lane, o, lse);
+        const int64_t off = b * p.o_stride_b + tok * p.o_stride_tok + h * p.o_stride_head + 4 * (lane & 15);
+        if (p.out_is_bf16) {
+            bf16x4 ob;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
-                *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + off) = ob;
-            } else {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o;
-            }
-            if (p.lse != nullptr && (lane & 15) == 0)
-                p.lse[b * p.lse_stride_b + tok * p.lse_stride_tok + h * p.lse_stride_head] = lse;
+            for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + off) = ob;
+        } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o;
         }
+        if (p.lse != nullptr && (lane & 15) == 0)
+            p.lse[b * p.lse_stride_b + tok * p.lse_stride_tok + h * p.lse_stride_head] = lse;
     }
     // Leave the counter at zero for the next call.
     if (threadIdx.x == 0) atomicExch(counter, 0u);

@@ -1,4 +1,4 @@
-"""CPU oracle for sink attention (float64, NumPy).
+"""CPU oracle for sink attention and the MoE routing softmax (float64, NumPy).
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
 ``cpu_baseline`` leg may import this package.  The HIP library's product path never imports it,
@@ -22,3 +22,4 @@ from .sink_attention import (  # noqa: F401
     sink_softmax,
     split_size,
 )
+from .moe_routing import moe_topk_softmax, topk_experts  # noqa: F401

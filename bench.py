@@ -18,10 +18,12 @@ The same JSON line also carries:
   KV length (sinkattn_prefill_split + sinkattn_decode_merge);
 * ``decode_multi``: the decode workload with T = 2, 4, 8 new tokens per sequence (the last T of the
   8192 keys), split + merge and single-launch, in KV GB/s;
+* ``moe_route``: MoE routing weights (top-4 of 128 experts, softmax over the chosen four) for 65,536
+  tokens of bf16 logits, in GB/s of logits read plus ids and weights written;
 * ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
-                      [--no-hot] [--no-multi]
+                      [--no-hot] [--no-multi] [--no-moe]
 """
 from __future__ import annotations
 
@@ -144,6 +146,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode detail")
+    ap.add_argument("--no-moe", action="store_true", help="skip the MoE routing detail")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the steps that reuse one K/V set (cache-resident; never the headline)")
     args = ap.parse_args()
@@ -412,6 +415,33 @@ def main():
             "split_tflops": round(a_flops / (ms_split * 1e-3) / 1e12, 2),
             "algorithmic_flop": a_flops,
         }
+
+    # ---------------------------------------------------------------- MoE routing softmax (detail)
+    if not args.no_moe:
+        tokens, experts, top_k = 65536, 128, 4
+        gen = torch.Generator().manual_seed(1008)
+        n_lsets = 8  # 8 x 16 MiB of logits: more than the Infinity Cache holds
+        logit_sets = [torch.randn((tokens, experts), generator=gen).to(torch.bfloat16).to(dev)
+                      for _ in range(n_lsets)]
+        ids = torch.empty((tokens, top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((tokens, top_k), dtype=torch.bfloat16, device=dev)
+
+        def route(i):
+            sa.moe_topk_softmax(logit_sets[i % n_lsets], top_k, ids=ids, weights=wts)
+
+        route(0)
+        ms_route = _time_graph(_capture(route, n_rep, torch), n_rep, torch)
+        r_bytes = tokens * experts * 2 + tokens * top_k * (4 + 2)
+        r_gbs = r_bytes / (ms_route * 1e-3) / 1e9
+        _log(f"MoE routing {tokens} x {experts} top-{top_k}: {ms_route * 1e3:.2f} us ({r_gbs:.0f} GB/s)")
+        result["moe_route"] = {
+            "workload": "moe_topk_softmax_t65536_e128_k4_bf16",
+            "us_per_call": round(ms_route * 1e3, 3),
+            "gbs": round(r_gbs, 1),
+            "frac_of_hbm_peak": round(r_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": r_bytes,
+        }
+        del logit_sets
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:

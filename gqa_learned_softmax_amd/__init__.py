@@ -16,7 +16,7 @@ from ._lib import SinkAttnError  # noqa: F401
 
 __all__ = ["prefill", "prefill_split", "prefill_kv_split", "decode_split", "decode_merge", "decode",
            "decode_fused", "decode_workspace", "decode_multi_split", "decode_multi", "decode_multi_fused",
-           "SinkAttnError", "version"]
+           "moe_topk_softmax", "SinkAttnError", "version"]
 
 
 def version() -> int:
@@ -174,3 +174,19 @@ def decode_multi_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, 
         int(num_chunks), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def moe_topk_softmax(logits, top_k, over_all_experts=False, ids=None, weights=None,
+                     weights_dtype=torch.bfloat16):
+    """``sinkattn_moe_topk_softmax``: logits [T, E]; returns (ids [T, K] int32, weights [T, K])."""
+    tokens = logits.shape[0]
+    if ids is None:
+        ids = torch.empty((tokens, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((tokens, top_k), dtype=weights_dtype, device=logits.device)
+    dev = _lib.require_device(logits, ids, weights)
+    d = [_lib.describe(t) for t in (logits, ids, weights)]
+    _lib.check(_lib.lib.sinkattn_moe_topk_softmax(
+        _lib.ref(d[0]), int(top_k), 1 if over_all_experts else 0, _lib.ref(d[1]), _lib.ref(d[2]),
+        _lib.stream_handle(dev)))
+    return ids, weights

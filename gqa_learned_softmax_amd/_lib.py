@@ -70,6 +70,7 @@ EXPORTS = {
     "sinkattn_decode_workspace_size": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int],
                                        ctypes.c_size_t),
     "sinkattn_decode_workspace_counter_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
+    "sinkattn_moe_topk_softmax": ([_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_void_p], ctypes.c_int),
     "sinkattn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sinkattn_last_error": ([], ctypes.c_char_p),
     "sinkattn_version": ([], ctypes.c_int),

@@ -741,6 +741,71 @@ sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
     return launched(sinkattn::launch_decode_merge(p, static_cast<hipStream_t>(stream)));
 }
 
+sinkattn_status sinkattn_moe_topk_softmax(const sinkattn_tensor* logits, int top_k, int over_all_experts,
+                                          const sinkattn_tensor* topk_ids,
+                                          const sinkattn_tensor* topk_weights, void* stream) {
+    g_last_error.clear();
+    SA_TRY(check_desc(logits, "logits", 2));
+    SA_TRY(check_desc(topk_ids, "topk_ids", 2));
+    SA_TRY(check_desc(topk_weights, "topk_weights", 2));
+    if (logits->dtype != SINKATTN_BF16 && logits->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "logits: dtype must be bf16 or f32");
+    SA_TRY(check_dtype(topk_ids, "topk_ids", SINKATTN_I32));
+    if (topk_weights->dtype != SINKATTN_BF16 && topk_weights->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "topk_weights: dtype must be bf16 or f32");
+    const int64_t tokens = logits->shape[0], experts = logits->shape[1];
+    if (top_k < 1) return fail(SINKATTN_ERR_SHAPE, "top_k must be >= 1 (got %d)", top_k);
+    if (topk_ids->shape[0] != tokens || topk_ids->shape[1] != top_k)
+        return fail(SINKATTN_ERR_SHAPE, "topk_ids: expected [T, top_k]");
+    if (topk_weights->shape[0] != tokens || topk_weights->shape[1] != top_k)
+        return fail(SINKATTN_ERR_SHAPE, "topk_weights: expected [T, top_k]");
+    if (experts < 1 || top_k > experts)
+        return fail(SINKATTN_ERR_SHAPE, "top_k (%d) must not exceed the expert count (%lld)", top_k,
+                    (long long)experts);
+    if (experts > 256 || top_k > 16)
+        return fail(SINKATTN_ERR_UNSUPPORTED, "at most 256 experts and top_k <= 16 (got %lld, %d)",
+                    (long long)experts, top_k);
+    if (tokens >= (int64_t(1) << 35))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    SA_TRY(check_data(logits, "logits"));
+    SA_TRY(check_data(topk_ids, "topk_ids"));
+    SA_TRY(check_data(topk_weights, "topk_weights"));
+    if (logits->stride[1] != 1 && experts > 1)
+        return fail(SINKATTN_ERR_LAYOUT, "logits: innermost stride must be 1");
+    if (reinterpret_cast<uintptr_t>(logits->data) % elem_size(logits->dtype) != 0)
+        return fail(SINKATTN_ERR_LAYOUT, "logits: data pointer not element-aligned");
+    const sinkattn_tensor* outs[2] = {topk_ids, topk_weights};
+    const char* onames[2] = {"topk_ids", "topk_weights"};
+    for (int a = 0; a < 2; ++a) {
+        if (outs[a]->stride[1] != 1 && outs[a]->shape[1] > 1)
+            return fail(SINKATTN_ERR_LAYOUT, "%s: innermost stride must be 1", onames[a]);
+        if (reinterpret_cast<uintptr_t>(outs[a]->data) % elem_size(outs[a]->dtype) != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "%s: data pointer not element-aligned", onames[a]);
+        SA_TRY(check_no_self_overlap(outs[a], onames[a]));
+        SA_TRY(check_disjoint(outs[a], onames[a], logits, "logits"));
+    }
+    SA_TRY(check_disjoint(topk_ids, "topk_ids", topk_weights, "topk_weights"));
+
+    if (tokens == 0) return SINKATTN_OK;
+    sinkattn::MoeTopkParams p{};
+    p.logits = logits->data;
+    p.ids = static_cast<int32_t*>(topk_ids->data);
+    p.weights = topk_weights->data;
+    p.logits_stride = logits->stride[0];
+    p.ids_stride = topk_ids->stride[0];
+    p.weights_stride = topk_weights->stride[0];
+    p.tokens = tokens;
+    p.experts = static_cast<int32_t>(experts);
+    p.top_k = top_k;
+    p.over_all = over_all_experts != 0;
+    p.logits_is_bf16 = logits->dtype == SINKATTN_BF16;
+    p.weights_is_bf16 = topk_weights->dtype == SINKATTN_BF16;
+    // 16-byte row loads only where every row starts on a 16-byte boundary.
+    p.vector_rows = reinterpret_cast<uintptr_t>(logits->data) % 16 == 0 &&
+                    (tokens == 1 || (logits->stride[0] * elem_size(logits->dtype)) % 16 == 0);
+    return launched(sinkattn::launch_moe_topk_softmax(p, static_cast<hipStream_t>(stream)));
+}
+
 const char* sinkattn_status_string(sinkattn_status status) {
     switch (status) {
         case SINKATTN_OK: return "ok";

@@ -88,6 +88,22 @@ struct DecodeMergeParams {
     int32_t out_is_bf16;
 };
 
+// MoE routing: logits [tokens, experts] (bf16 or f32, row stride in elements); per token the
+// top_k expert ids (int32) and weights (bf16 or f32), rows of stride ids_stride / weights_stride.
+struct MoeTopkParams {
+    const void* logits;
+    int32_t* ids;
+    void* weights;
+    int64_t logits_stride, ids_stride, weights_stride;
+    int64_t tokens;
+    int32_t experts;      // 1 .. 256
+    int32_t top_k;        // 1 .. min(experts, 16)
+    int32_t over_all;     // nonzero: normalise over all experts instead of the chosen K
+    int32_t logits_is_bf16;
+    int32_t weights_is_bf16;
+    int32_t vector_rows;  // every logits row starts 16-byte aligned
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream);
@@ -95,5 +111,6 @@ hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t strea
 // Split and merge in one launch (bf16); partials and counters as in DecodeSplitParams.
 hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream);
+hipError_t launch_moe_topk_softmax(const MoeTopkParams& p, hipStream_t stream);
 
 }  // namespace sinkattn

@@ -1,6 +1,7 @@
 /*
  * sinkattn.h - C ABI of libsinkattn: grouped-query attention with a learned per-head softmax sink,
- * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ * and the MoE routing softmax of the same model, hand-written HIP kernels for AMD Instinct MI355X
+ * (gfx950).
  *
  * The operation (blog post "GPT-OSS on Day 0", Perplexity, 2025; section "Kernels for GPT-OSS",
  * subsection "Sink attention"): every query head h owns one learned scalar sink[h]. For a query
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_VERSION 4
+#define SINKATTN_VERSION 5
 
 typedef enum {
     SINKATTN_OK = 0,
@@ -274,6 +275,27 @@ size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_
 /* Bytes at the start of that workspace holding the counters that must start at zero. */
 size_t sinkattn_decode_workspace_counter_bytes(int64_t batch, int64_t num_kv_heads);
 
+/*
+ * sinkattn_moe_topk_softmax - MoE routing weights: the top-K experts of every token and a softmax
+ * taken over the K chosen logits only.
+ *
+ * Source: "GPT-OSS on Day 0" (Perplexity): the model outline ("GPT-OSS on Hopper") lists a softmax
+ * after the top-K choice for the expert weights; section "Kernels for GPT-OSS" says the routing
+ * scores take the softmax over the top-K chosen experts only, unlike DeepSeek-style models that
+ * take it over all experts, and that computing the expert weights in bfloat16 matters for accuracy.
+ *
+ *   logits        [T, E]  bf16 | fp32   router logits (finite or -inf; no NaN), unit inner stride
+ *   top_k         K, 1 <= K <= min(E, 16); E <= 256
+ *   over_all_experts  zero: weights = softmax over the K chosen logits (each row sums to 1);
+ *                 nonzero: softmax over all E logits, the K chosen entries of it (the contrast mode)
+ *   topk_ids      [T, K] int32   chosen experts, by logit descending; among equal logits the lower
+ *                                expert index comes first
+ *   topk_weights  [T, K] bf16 | fp32   computed in fp32, stored rounded to nearest (bf16)
+ * A row whose largest logit is -inf gets weights 0. T = 0 launches nothing.
+ */
+sinkattn_status sinkattn_moe_topk_softmax(const sinkattn_tensor* logits, int top_k, int over_all_experts,
+                                          const sinkattn_tensor* topk_ids,
+                                          const sinkattn_tensor* topk_weights, void* stream);
 /* Short static description of a status code. Never NULL. */
 const char* sinkattn_status_string(sinkattn_status status);
 

@@ -427,3 +427,50 @@ def test_multi_fused_rejects(name, mutate, code):
     status = call_mfused(mutate(mfused_args()))
     assert status == code, (status, last_error())
     assert last_error()
+
+
+# ----------------------------------------------------------------------------- MoE routing softmax
+def moe_args(t=32, e=128, k=4, dtype=BF16, wdtype=BF16):
+    return dict(logits=T([t, e], dtype), k=k, all=0, ids=T([t, k], I32), w=T([t, k], wdtype))
+
+
+def call_moe(a):
+    return _lib.lib.sinkattn_moe_topk_softmax(R(a["logits"]), a["k"], a["all"], R(a["ids"]), R(a["w"]), None)
+
+
+def test_moe_empty_is_ok():
+    assert call_moe(moe_args(t=0)) == _lib.OK
+
+
+def test_moe_accepts_unaligned_rows():
+    # 100 bf16 experts: 200-byte rows; element loads serve them (nothing launched for T = 0)
+    assert call_moe(dict(moe_args(t=0, e=100), logits=T([0, 100], strides=[100, 1]))) == _lib.OK
+
+
+MOE_CASES = [
+    ("logits_null", lambda a: _mut(a, logits=None), _lib.ERR_NULL),
+    ("ids_null", lambda a: _mut(a, ids=None), _lib.ERR_NULL),
+    ("logits_i32", lambda a: _mut(a, logits=T([32, 128], I32)), _lib.ERR_DTYPE),
+    ("ids_f32", lambda a: _mut(a, ids=T([32, 4], F32)), _lib.ERR_DTYPE),
+    ("weights_i32", lambda a: _mut(a, w=T([32, 4], I32)), _lib.ERR_DTYPE),
+    ("k_zero", lambda a: moe_args(k=0), _lib.ERR_SHAPE),
+    ("k_over_e", lambda a: moe_args(e=3, k=4), _lib.ERR_SHAPE),
+    ("ids_rows", lambda a: _mut(a, ids=T([31, 4], I32)), _lib.ERR_SHAPE),
+    ("weights_cols", lambda a: _mut(a, w=T([32, 5], BF16)), _lib.ERR_SHAPE),
+    ("logits_rank3", lambda a: _mut(a, logits=T([2, 16, 128])), _lib.ERR_SHAPE),
+    ("e_over_256", lambda a: moe_args(e=257), _lib.ERR_UNSUPPORTED),
+    ("k_over_16", lambda a: moe_args(e=64, k=17), _lib.ERR_UNSUPPORTED),
+    ("logits_inner_stride", lambda a: _mut(a, logits=T([32, 128], strides=[256, 2])), _lib.ERR_LAYOUT),
+    ("logits_misaligned", lambda a: _mut(a, logits=T([32, 128], addr=(7 << 44) + 1)), _lib.ERR_LAYOUT),
+    ("ids_inner_stride", lambda a: _mut(a, ids=T([32, 4], I32, strides=[8, 2])), _lib.ERR_LAYOUT),
+    ("weights_overlap_rows", lambda a: _mut(a, w=T([32, 4], BF16, strides=[2, 1])), _lib.ERR_LAYOUT),
+    ("ids_overlap_weights", lambda a: _mut(a, ids=T([32, 4], I32, addr=a["w"].data)), _lib.ERR_LAYOUT),
+    ("weights_overlap_logits", lambda a: _mut(a, w=T([32, 4], BF16, addr=a["logits"].data + 64)), _lib.ERR_LAYOUT),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", MOE_CASES, ids=[c[0] for c in MOE_CASES])
+def test_moe_rejects(name, mutate, code):
+    status = call_moe(mutate(moe_args()))
+    assert status == code, (status, last_error())
+    assert last_error()

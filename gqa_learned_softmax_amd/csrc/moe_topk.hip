@@ -240,17 +240,23 @@ __global__ __launch_bounds__(kMoeThreads) void moe_topk_softmax_kernel(MoeTopkPa
         }
     }
 
-    // Softmax in fp32 relative to the largest logit; no finite logit means no weight.
+    // Softmax in fp32 relative to the largest logit; no finite logit means no weight. bf16 weights
+    // use the hardware exp2 and reciprocal (their error, ~1e-6 relative, is far below the bf16
+    // rounding that follows); fp32 weights keep the correctly rounded expf and division.
     const bool live = top != kNegInf;
-    const float w_num = live && j < p.top_k ? expf(my_v - top) : 0.0f;
+    const bool fast = p.weights_is_bf16;
+    const float w_num = live && j < p.top_k ? (fast ? exp2_fast((my_v - top) * kLog2e) : expf(my_v - top)) : 0.0f;
     float denom = w_num;
     if (p.over_all) {
         denom = 0.0f;
 #pragma unroll
-        for (int e = 0; e < V; ++e) denom += live & (j * V + e < p.experts) ? expf(x[e] - top) : 0.0f;
+        for (int e = 0; e < V; ++e) {
+            const float d = x[e] - top;
+            denom += live & (j * V + e < p.experts) ? (fast ? exp2_fast(d * kLog2e) : expf(d)) : 0.0f;
+        }
     }
     denom = group_sum(denom);
-    const float w = live ? w_num / denom : 0.0f;
+    const float w = !live ? 0.0f : fast ? w_num * __builtin_amdgcn_rcpf(denom) : w_num / denom;
 
     if (j < p.top_k) {
         p.ids[row * p.ids_stride + j] = my_i;

@@ -1,4 +1,5 @@
-"""CPU oracle for sink attention and the MoE routing softmax (float64, NumPy).
+"""CPU oracle for sink attention, the MoE routing softmax and the bias / FP8 block-scaled GEMM
+(float64, NumPy).
 
 TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
 ``cpu_baseline`` leg may import this package.  The HIP library's product path never imports it,
@@ -23,3 +24,4 @@ from .sink_attention import (  # noqa: F401
     split_size,
 )
 from .moe_routing import moe_topk_softmax, topk_experts  # noqa: F401
+from .gemm import e4m3_to_float, gemm_bias, gemm_fp8_block_scaled  # noqa: F401

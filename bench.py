@@ -20,10 +20,13 @@ The same JSON line also carries:
   8192 keys), split + merge and single-launch, in KV GB/s;
 * ``moe_route``: MoE routing weights (top-4 of 128 experts, softmax over the chosen four) for 65,536
   tokens of bf16 logits, in GB/s of logits read plus ids and weights written;
+* ``linear``: the linear layer with the bias in the accumulators, M = N = K = 4096, bf16 and FP8 with
+  128 x 128 block scaling, TFLOP/s against the dense MFMA peaks (torch's bf16 linear timed beside it
+  as context);
 * ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
-                      [--no-hot] [--no-multi] [--no-moe]
+                      [--no-hot] [--no-multi] [--no-moe] [--no-linear]
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
 METRIC = "decode KV GB/s (% of HBM peak) + prefill TFLOP/s (% of bf16 MFMA peak)"
 ROTATE_BYTES = 512 * 2**20
 CALIB_BYTES = 256 * 2**20
@@ -147,6 +151,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode detail")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE routing detail")
+    ap.add_argument("--no-linear", action="store_true", help="skip the linear-layer detail")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the steps that reuse one K/V set (cache-resident; never the headline)")
     args = ap.parse_args()
@@ -442,6 +447,50 @@ def main():
             "algorithmic_bytes": r_bytes,
         }
         del logit_sets
+
+    # ---------------------------------------------------------------- linear layers (detail)
+    if not args.no_linear:
+        gm = gn = gk = 4096
+        gen = torch.Generator().manual_seed(1009)
+        lx = torch.randn((gm, gk), generator=gen).to(torch.bfloat16).to(dev)
+        lw = torch.randn((gn, gk), generator=gen).to(torch.bfloat16).to(dev)
+        lb = torch.randn(gn, generator=gen).to(dev)
+        ly = torch.empty((gm, gn), dtype=torch.bfloat16, device=dev)
+        qx = (torch.randn((gm, gk), generator=gen) * 2).to(torch.float8_e4m3fn).to(dev)
+        qw = (torch.randn((gn, gk), generator=gen) * 2).to(torch.float8_e4m3fn).to(dev)
+        qsx = (torch.rand((gm, gk // 128), generator=gen) + 0.5).to(dev)
+        qsw = (torch.rand((gn // 128, gk // 128), generator=gen) * 0.1 + 0.01).to(dev)
+        n_lin = max(10, args.steps // 2)
+        gflop = 2.0 * gm * gn * gk
+
+        def lin_bf16(i):
+            sa.linear_bias(lx, lw, lb, out=ly)
+
+        def lin_fp8(i):
+            sa.linear_fp8_block_scaled(qx, qsx, qw, qsw, lb, out=ly)
+
+        def lin_torch(i):
+            torch.nn.functional.linear(lx, lw, lb.to(torch.bfloat16))
+
+        lin_bf16(0)
+        lin_fp8(0)
+        lin_torch(0)
+        ms_lb = _time_graph(_capture(lin_bf16, n_lin, torch), n_lin, torch)
+        ms_lf = _time_graph(_capture(lin_fp8, n_lin, torch), n_lin, torch)
+        ms_lt = _time_graph(_capture(lin_torch, n_lin, torch), n_lin, torch)
+        tf_b, tf_f, tf_t = (gflop / (ms * 1e-3) / 1e12 for ms in (ms_lb, ms_lf, ms_lt))
+        _log(f"linear 4096^3: bf16+bias {ms_lb * 1e3:.1f} us ({tf_b:.0f} TFLOP/s), fp8 block-scaled "
+             f"{ms_lf * 1e3:.1f} us ({tf_f:.0f} TFLOP/s); torch bf16 linear {ms_lt * 1e3:.1f} us ({tf_t:.0f})")
+        result["linear"] = {
+            "workload": "linear_m4096_n4096_k4096_bias",
+            "bf16_us": round(ms_lb * 1e3, 2), "bf16_tflops": round(tf_b, 1),
+            "bf16_frac_of_mfma_peak": round(tf_b / BF16_MFMA_PEAK_TFLOPS, 4),
+            "fp8_block_scaled_us": round(ms_lf * 1e3, 2), "fp8_tflops": round(tf_f, 1),
+            "fp8_frac_of_mfma_peak": round(tf_f / FP8_MFMA_PEAK_TFLOPS, 4),
+            "torch_bf16_linear_us": round(ms_lt * 1e3, 2),
+            "algorithmic_flop": gflop,
+        }
+        del lx, lw, qx, qw
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:

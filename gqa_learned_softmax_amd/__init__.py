@@ -16,7 +16,7 @@ from ._lib import SinkAttnError  # noqa: F401
 
 __all__ = ["prefill", "prefill_split", "prefill_kv_split", "decode_split", "decode_merge", "decode",
            "decode_fused", "decode_workspace", "decode_multi_split", "decode_multi", "decode_multi_fused",
-           "moe_topk_softmax", "SinkAttnError", "version"]
+           "moe_topk_softmax", "linear_bias", "linear_fp8_block_scaled", "SinkAttnError", "version"]
 
 
 def version() -> int:
@@ -190,3 +190,27 @@ def moe_topk_softmax(logits, top_k, over_all_experts=False, ids=None, weights=No
         _lib.ref(d[0]), int(top_k), 1 if over_all_experts else 0, _lib.ref(d[1]), _lib.ref(d[2]),
         _lib.stream_handle(dev)))
     return ids, weights
+
+
+def linear_bias(x, w, bias=None, out=None, out_dtype=torch.bfloat16):
+    """``sinkattn_linear_bias``: y [M, N] = x [M, K] w[N, K]^T + bias [N] (bf16 operands)."""
+    if out is None:
+        out = torch.empty((x.shape[0], w.shape[0]), dtype=out_dtype, device=x.device)
+    dev = _lib.require_device(x, w, bias, out)
+    d = [_lib.describe(t) for t in (x, w, bias, out)]
+    _lib.check(_lib.lib.sinkattn_linear_bias(_lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]),
+                                             _lib.stream_handle(dev)))
+    return out
+
+
+def linear_fp8_block_scaled(x, scale_x, w, scale_w, bias=None, out=None, out_dtype=torch.bfloat16):
+    """``sinkattn_linear_fp8_block_scaled``: x [M, K], w [N, K] float8_e4m3fn; scale_x [M, K/128],
+    scale_w [ceil(N/128), K/128] fp32; y [M, N]."""
+    if out is None:
+        out = torch.empty((x.shape[0], w.shape[0]), dtype=out_dtype, device=x.device)
+    dev = _lib.require_device(x, scale_x, w, scale_w, bias, out)
+    d = [_lib.describe(t) for t in (x, scale_x, w, scale_w, bias, out)]
+    _lib.check(_lib.lib.sinkattn_linear_fp8_block_scaled(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]), _lib.ref(d[5]),
+        _lib.stream_handle(dev)))
+    return out

@@ -26,7 +26,8 @@ ERR_LAUNCH = 6
 F32 = 0
 BF16 = 1
 I32 = 2
-_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}
+FP8_E4M3 = 3
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32, torch.float8_e4m3fn: FP8_E4M3}
 _UNKNOWN_DTYPE = 99  # the library rejects it with SINKATTN_ERR_DTYPE
 
 
@@ -71,6 +72,8 @@ EXPORTS = {
                                        ctypes.c_size_t),
     "sinkattn_decode_workspace_counter_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),
     "sinkattn_moe_topk_softmax": ([_P, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_void_p], ctypes.c_int),
+    "sinkattn_linear_bias": ([_P, _P, _P, _P, ctypes.c_void_p], ctypes.c_int),
+    "sinkattn_linear_fp8_block_scaled": ([_P, _P, _P, _P, _P, _P, ctypes.c_void_p], ctypes.c_int),
     "sinkattn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sinkattn_last_error": ([], ctypes.c_char_p),
     "sinkattn_version": ([], ctypes.c_int),

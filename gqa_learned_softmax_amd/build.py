@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libsinkattn.so")
 
-SOURCES = ["api.cpp", "decode_split.hip", "decode_merge.hip", "prefill.hip", "moe_topk.hip"]
+SOURCES = ["api.cpp", "decode_split.hip", "decode_merge.hip", "prefill.hip", "moe_topk.hip", "gemm.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

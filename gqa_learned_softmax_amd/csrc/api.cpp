@@ -37,6 +37,7 @@ int64_t elem_size(sinkattn_dtype dt) {
         case SINKATTN_F32: return 4;
         case SINKATTN_BF16: return 2;
         case SINKATTN_I32: return 4;
+        case SINKATTN_FP8_E4M3: return 1;
     }
     return 0;
 }
@@ -46,6 +47,7 @@ const char* dtype_name(sinkattn_dtype dt) {
         case SINKATTN_F32: return "f32";
         case SINKATTN_BF16: return "bf16";
         case SINKATTN_I32: return "i32";
+        case SINKATTN_FP8_E4M3: return "fp8_e4m3";
     }
     return "?";
 }
@@ -53,7 +55,8 @@ const char* dtype_name(sinkattn_dtype dt) {
 // Descriptor sanity: non-null, known dtype, expected rank, non-negative extents and strides.
 sinkattn_status check_desc(const sinkattn_tensor* t, const char* name, int ndim) {
     if (t == nullptr) return fail(SINKATTN_ERR_NULL, "%s: descriptor is NULL", name);
-    if (t->dtype != SINKATTN_F32 && t->dtype != SINKATTN_BF16 && t->dtype != SINKATTN_I32)
+    if (t->dtype != SINKATTN_F32 && t->dtype != SINKATTN_BF16 && t->dtype != SINKATTN_I32 &&
+        t->dtype != SINKATTN_FP8_E4M3)
         return fail(SINKATTN_ERR_DTYPE, "%s: unknown dtype code %d", name, (int)t->dtype);
     if (t->ndim != ndim)
         return fail(SINKATTN_ERR_SHAPE, "%s: rank %d, expected %d", name, t->ndim, ndim);
@@ -518,6 +521,99 @@ sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tenso
     return launched(sinkattn::launch_decode_merge(mp, s));
 }
 
+// sinkattn_linear_bias (bf16) and sinkattn_linear_fp8_block_scaled (FP8 with block scales).
+sinkattn_status linear_impl(const sinkattn_tensor* x, const sinkattn_tensor* scale_x,
+                            const sinkattn_tensor* w, const sinkattn_tensor* scale_w,
+                            const sinkattn_tensor* bias, const sinkattn_tensor* y, void* stream, bool fp8) {
+    g_last_error.clear();
+    SA_TRY(check_desc(x, "x", 2));
+    SA_TRY(check_desc(w, "w", 2));
+    SA_TRY(check_desc(y, "y", 2));
+    if (bias != nullptr) SA_TRY(check_desc(bias, "bias", 1));
+    if (fp8) {
+        SA_TRY(check_desc(scale_x, "scale_x", 2));
+        SA_TRY(check_desc(scale_w, "scale_w", 2));
+    }
+    const sinkattn_dtype in = fp8 ? SINKATTN_FP8_E4M3 : SINKATTN_BF16;
+    SA_TRY(check_dtype(x, "x", in));
+    SA_TRY(check_dtype(w, "w", in));
+    if (y->dtype != SINKATTN_BF16 && y->dtype != SINKATTN_F32)
+        return fail(SINKATTN_ERR_DTYPE, "y: dtype must be bf16 or f32");
+    if (bias != nullptr) SA_TRY(check_dtype(bias, "bias", SINKATTN_F32));
+    if (fp8) {
+        SA_TRY(check_dtype(scale_x, "scale_x", SINKATTN_F32));
+        SA_TRY(check_dtype(scale_w, "scale_w", SINKATTN_F32));
+    }
+    const int64_t m = x->shape[0], k = x->shape[1], n = w->shape[0];
+    const int64_t step = fp8 ? 128 : 64;
+    if (w->shape[1] != k) return fail(SINKATTN_ERR_SHAPE, "w: expected [N, K] with the K of x");
+    if (y->shape[0] != m || y->shape[1] != n) return fail(SINKATTN_ERR_SHAPE, "y: expected [M, N]");
+    if (bias != nullptr && bias->shape[0] != n) return fail(SINKATTN_ERR_SHAPE, "bias: expected [N]");
+    if (k <= 0 || k % step != 0)
+        return fail(SINKATTN_ERR_SHAPE, "K (%lld) must be a positive multiple of %lld", (long long)k,
+                    (long long)step);
+    if (fp8) {
+        if (scale_x->shape[0] != m || scale_x->shape[1] != k / 128)
+            return fail(SINKATTN_ERR_SHAPE, "scale_x: expected [M, K/128]");
+        if (scale_w->shape[0] != (n + 127) / 128 || scale_w->shape[1] != k / 128)
+            return fail(SINKATTN_ERR_SHAPE, "scale_w: expected [ceil(N/128), K/128]");
+    }
+    const int64_t es = elem_size(in);
+    if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31) ||
+        ((m + 127) / 128) * ((n + 127) / 128) >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    // A work-group addresses its 128 rows of x and of w with 32-bit byte offsets.
+    if (128 * x->stride[0] * es >= (int64_t(1) << 31) || 128 * w->stride[0] * es >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "row stride too large (128 rows must span < 2 GiB)");
+    SA_TRY(check_data(x, "x"));
+    SA_TRY(check_data(w, "w"));
+    SA_TRY(check_data(y, "y"));
+    if (bias != nullptr) SA_TRY(check_data(bias, "bias"));
+    if (fp8) {
+        SA_TRY(check_data(scale_x, "scale_x"));
+        SA_TRY(check_data(scale_w, "scale_w"));
+    }
+    SA_TRY(check_rows(x, "x"));
+    SA_TRY(check_rows(w, "w"));
+    if ((m > 1 && x->stride[0] < k) || (n > 1 && w->stride[0] < k))
+        return fail(SINKATTN_ERR_LAYOUT, "x/w: rows overlap (row stride below K)");
+    if (bias != nullptr && bias->stride[0] != 1 && n > 1)
+        return fail(SINKATTN_ERR_LAYOUT, "bias: must be contiguous");
+    if (y->stride[1] != 1 && n > 1) return fail(SINKATTN_ERR_LAYOUT, "y: innermost stride must be 1");
+    const sinkattn_tensor* aligned[4] = {bias, y, scale_x, scale_w};
+    const char* anames[4] = {"bias", "y", "scale_x", "scale_w"};
+    for (int a = 0; a < 4; ++a)
+        if (aligned[a] != nullptr && reinterpret_cast<uintptr_t>(aligned[a]->data) % elem_size(aligned[a]->dtype) != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "%s: data pointer not element-aligned", anames[a]);
+    SA_TRY(check_no_self_overlap(y, "y"));
+    const sinkattn_tensor* ins[5] = {x, w, bias, scale_x, scale_w};
+    const char* inames[5] = {"x", "w", "bias", "scale_x", "scale_w"};
+    for (int b = 0; b < 5; ++b)
+        if (ins[b] != nullptr) SA_TRY(check_disjoint(y, "y", ins[b], inames[b]));
+
+    if (m == 0 || n == 0) return SINKATTN_OK;
+    sinkattn::GemmParams p{};
+    p.x = x->data;
+    p.w = w->data;
+    p.bias = bias != nullptr ? static_cast<const float*>(bias->data) : nullptr;
+    p.y = y->data;
+    p.scale_x = fp8 ? static_cast<const float*>(scale_x->data) : nullptr;
+    p.scale_w = fp8 ? static_cast<const float*>(scale_w->data) : nullptr;
+    // A single row's stride is never stepped: the buffer range then spans just its K elements.
+    p.ldx = m > 1 ? x->stride[0] : k;
+    p.ldw = n > 1 ? w->stride[0] : k;
+    p.ldy = y->stride[0];
+    p.sx_stride_m = fp8 ? scale_x->stride[0] : 0;
+    p.sx_stride_kb = fp8 ? scale_x->stride[1] : 0;
+    p.sw_stride_nb = fp8 ? scale_w->stride[0] : 0;
+    p.sw_stride_kb = fp8 ? scale_w->stride[1] : 0;
+    p.m = static_cast<int32_t>(m);
+    p.n = static_cast<int32_t>(n);
+    p.k = static_cast<int32_t>(k);
+    p.y_is_bf16 = y->dtype == SINKATTN_BF16;
+    return launched(sinkattn::launch_gemm_bias(p, fp8, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -804,6 +900,19 @@ sinkattn_status sinkattn_moe_topk_softmax(const sinkattn_tensor* logits, int top
     p.vector_rows = reinterpret_cast<uintptr_t>(logits->data) % 16 == 0 &&
                     (tokens == 1 || (logits->stride[0] * elem_size(logits->dtype)) % 16 == 0);
     return launched(sinkattn::launch_moe_topk_softmax(p, static_cast<hipStream_t>(stream)));
+}
+
+sinkattn_status sinkattn_linear_bias(const sinkattn_tensor* x, const sinkattn_tensor* w,
+                                     const sinkattn_tensor* bias, const sinkattn_tensor* y,
+                                     void* stream) {
+    return linear_impl(x, nullptr, w, nullptr, bias, y, stream, false);
+}
+
+sinkattn_status sinkattn_linear_fp8_block_scaled(const sinkattn_tensor* x, const sinkattn_tensor* scale_x,
+                                                 const sinkattn_tensor* w, const sinkattn_tensor* scale_w,
+                                                 const sinkattn_tensor* bias, const sinkattn_tensor* y,
+                                                 void* stream) {
+    return linear_impl(x, scale_x, w, scale_w, bias, y, stream, true);
 }
 
 const char* sinkattn_status_string(sinkattn_status status) {

@@ -1,0 +1,224 @@
+// Linear layer with a bias folded into the matrix-core accumulators (gfx950):
+//   Y[M, N] = X[M, K] W[N, K]^T + bias[N], in bf16, or in FP8 (OCP E4M3) with 128 x 128 block scaling.
+//
+// Source: "GPT-OSS on Day 0" (Perplexity). Section "GPT-OSS on Hopper" picks FP8 with 128x128 block
+// scaling and a bias term for the GEMM kernels; section "Kernels for GPT-OSS" adds the bias by
+// starting the accumulator registers at bias values loaded from memory once per output block. Here
+// every 32x32 accumulator block starts at the bias: a lane's 16 accumulators share one output
+// column (the MFMA C layout), so the bias costs one load per lane and block and no epilogue pass.
+//
+// Work-group: a 128 x 128 output tile, four waves of 64 x 64 (2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, or of v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales for FP8).
+// Each K step stages 128 bytes of every A and B row (64 bf16 or 128 FP8 values = one scale block)
+// in double-buffered LDS tiles of pitch 144 bytes (16-byte reads of 16 consecutive rows hit disjoint
+// banks); the next step's loads are in flight while the current one is multiplied. FP8: each
+// 128-wide k block is multiplied into a temporary accumulator, then added to the running one times
+// scale_x[row, kb] * scale_w[column block, kb] (rows' scales staged in LDS with the tile).
+// Tiles are spread XCD-aware: each XCD takes a contiguous range of tile indices, walked in groups of
+// 8 tile-rows so the X and W panels a group shares stay in that XCD's L2.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace sinkattn {
+namespace {
+
+constexpr int kGemmThreads = 256;
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+constexpr int kStepBytes = 128;    // bytes of each row staged per K step
+constexpr int kRowPitch = 144;     // LDS row pitch in bytes
+constexpr int kGroupRows = 8;      // tile-rows per group in the tile order
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct GemmStage {
+    i32x4 a[4];
+    i32x4 b[4];
+    float sx;  // FP8: this thread's row scale (threads < 128)
+};
+
+template <bool kFp8>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileM][kRowPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kTileN][kRowPitch];
+    __shared__ __attribute__((aligned(16))) float sx_lds[2][kTileM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r32 = lane & 31, h = lane >> 5;
+
+    // Tile order: contiguous ranges per XCD (work-groups go round-robin over the 8 XCDs), grouped.
+    const int tiles_m = (p.m + kTileM - 1) / kTileM;
+    const int tiles_n = (p.n + kTileN - 1) / kTileN;
+    const int tiles = tiles_m * tiles_n;
+    int t = blockIdx.x;
+    if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
+    const int per_group = kGroupRows * tiles_n;
+    const int first_m = (t / per_group) * kGroupRows;
+    const int group_rows = tiles_m - first_m < kGroupRows ? tiles_m - first_m : kGroupRows;
+    const int tm = first_m + (t % per_group) % group_rows;
+    const int tn = (t % per_group) / group_rows;
+    const int m0 = tm * kTileM, n0 = tn * kTileN;
+
+    // Operand slices of this work-group; rows past M or N load as zeros (buffer range).
+    const int es = kFp8 ? 1 : 2;
+    const int rows_a = p.m - m0 < kTileM ? p.m - m0 : kTileM;
+    const int rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
+    const uint32_t lda = static_cast<uint32_t>(p.ldx * es), ldb = static_cast<uint32_t>(p.ldw * es);
+    const __amdgpu_buffer_rsrc_t ars =
+        make_buffer(static_cast<const uint8_t*>(p.x) + static_cast<int64_t>(m0) * lda, rows_a * lda);
+    const __amdgpu_buffer_rsrc_t brs =
+        make_buffer(static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(n0) * ldb, rows_b * ldb);
+
+    // Accumulators start at the bias of their column (lane column r32 of each 32x32 block).
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) {
+        const int n = n0 + 64 * wn + 32 * bn + r32;
+        const float b = p.bias != nullptr && n < p.n ? p.bias[n] : 0.0f;
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[bm][bn][i] = b;
+    }
+
+    // Thread piece j: row (tid + 256 j) / 8, 16-byte segment (tid + 256 j) % 8 of the step's bytes.
+    auto stage_load = [&](GemmStage& s, int step) {
+        const uint32_t kb = static_cast<uint32_t>(step) * kStepBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = tid + kGemmThreads * j;
+            const uint32_t row = piece >> 3, seg = piece & 7;
+            s.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, row * lda + kb + 16 * seg, 0, 0));
+            s.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, row * ldb + kb + 16 * seg, 0, 0));
+        }
+        if constexpr (kFp8) {
+            const int row = m0 + tid;
+            s.sx = tid < kTileM && row < p.m ? p.scale_x[row * p.sx_stride_m + step * p.sx_stride_kb] : 0.0f;
+        }
+    };
+    auto stage_store = [&](const GemmStage& s, int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = tid + kGemmThreads * j;
+            const int row = piece >> 3, seg = piece & 7;
+            *reinterpret_cast<i32x4*>(&a_lds[buf][row][16 * seg]) = s.a[j];
+            *reinterpret_cast<i32x4*>(&b_lds[buf][row][16 * seg]) = s.b[j];
+        }
+        if constexpr (kFp8)
+            if (tid < kTileM) sx_lds[buf][tid] = s.sx;
+    };
+    auto compute = [&](int buf, int step) {
+        const uint8_t* arow[2];
+        const uint8_t* brow[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            arow[q] = &a_lds[buf][64 * wm + 32 * q + r32][0];
+            brow[q] = &b_lds[buf][64 * wn + 32 * q + r32][0];
+        }
+        if constexpr (!kFp8) {
+            // Four k slices of 16 bf16; lane half h takes k 8h .. 8h + 7 of each slice.
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 av[2], bv[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    av[q] = *reinterpret_cast<const bf16x8*>(arow[q] + 32 * kk + 16 * h);
+                    bv[q] = *reinterpret_cast<const bf16x8*>(brow[q] + 32 * kk + 16 * h);
+                }
+#pragma unroll
+                for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+                    for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = mfma32x32x16(av[bm], bv[bn], acc[bm][bn]);
+            }
+        } else {
+            // Two k slices of 64 FP8; lane half h takes bytes 32h .. 32h + 31 of each slice (the
+            // same bytes for A and B, so the product pairs equal k whatever order the unit uses).
+            f32x16 part[2][2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                i32x8 av[2], bv[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow[q] + 64 * s + 32 * h);
+                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow[q] + 64 * s + 32 * h + 16);
+                    const i32x4 b0 = *reinterpret_cast<const i32x4*>(brow[q] + 64 * s + 32 * h);
+                    const i32x4 b1 = *reinterpret_cast<const i32x4*>(brow[q] + 64 * s + 32 * h + 16);
+                    av[q] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    bv[q] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+                    for (int bn = 0; bn < 2; ++bn)
+                        part[bm][bn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            av[bm], bv[bn], s == 0 ? zero_f32x16() : part[bm][bn], 0, 0, 0, 127, 0, 127);
+            }
+            // Promote: acc += part * scale_x[row] * scale_w (one weight scale per 128-column tile).
+            const float sw = p.scale_w[static_cast<int64_t>(tn) * p.sw_stride_nb + step * p.sw_stride_kb];
+#pragma unroll
+            for (int bm = 0; bm < 2; ++bm) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 sx4 = *reinterpret_cast<const f32x4*>(&sx_lds[buf][64 * wm + 32 * bm + 8 * g + 4 * h]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float c = sx4[e] * sw;
+#pragma unroll
+                        for (int bn = 0; bn < 2; ++bn)
+                            acc[bm][bn][4 * g + e] = fmaf(part[bm][bn][4 * g + e], c, acc[bm][bn][4 * g + e]);
+                    }
+                }
+            }
+        }
+    };
+
+    // One step ahead: step i + 1's loads are in flight while step i is multiplied, then go from
+    // registers into the other buffer; one barrier per step.
+    const int steps = p.k / (kStepBytes / es);
+    GemmStage st;
+    stage_load(st, 0);
+    stage_store(st, 0);
+    __syncthreads();
+    for (int i = 0; i < steps; ++i) {
+        if (i + 1 < steps) stage_load(st, i + 1);
+        compute(i & 1, i);
+        if (i + 1 < steps) stage_store(st, (i + 1) & 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane column r32 of each block, rows 8 (i / 4) + 4 h + (i % 4).
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn) {
+            const int n = n0 + 64 * wn + 32 * bn + r32;
+            if (n >= p.n) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + 64 * wm + 32 * bm + 8 * (i / 4) + 4 * h + (i % 4);
+                if (m >= p.m) continue;
+                const int64_t off = static_cast<int64_t>(m) * p.ldy + n;
+                if (p.y_is_bf16)
+                    static_cast<__bf16*>(p.y)[off] = static_cast<__bf16>(acc[bm][bn][i]);
+                else
+                    static_cast<float*>(p.y)[off] = acc[bm][bn][i];
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bias(const GemmParams& p, bool fp8, hipStream_t stream) {
+    const int64_t tiles = static_cast<int64_t>((p.m + kTileM - 1) / kTileM) * ((p.n + kTileN - 1) / kTileN);
+    if (fp8)
+        gemm_bias_kernel<true><<<dim3(static_cast<unsigned>(tiles)), dim3(kGemmThreads), 0, stream>>>(p);
+    else
+        gemm_bias_kernel<false><<<dim3(static_cast<unsigned>(tiles)), dim3(kGemmThreads), 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace sinkattn

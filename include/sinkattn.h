@@ -1,7 +1,7 @@
 /*
  * sinkattn.h - C ABI of libsinkattn: grouped-query attention with a learned per-head softmax sink,
- * and the MoE routing softmax of the same model, hand-written HIP kernels for AMD Instinct MI355X
- * (gfx950).
+ * and the MoE routing softmax and bias / FP8 block-scaled linear layers of the same model,
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
  *
  * The operation (blog post "GPT-OSS on Day 0", Perplexity, 2025; section "Kernels for GPT-OSS",
  * subsection "Sink attention"): every query head h owns one learned scalar sink[h]. For a query
@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_VERSION 5
+#define SINKATTN_VERSION 6
 
 typedef enum {
     SINKATTN_OK = 0,
@@ -65,7 +65,8 @@ typedef enum {
 typedef enum {
     SINKATTN_F32 = 0,
     SINKATTN_BF16 = 1,
-    SINKATTN_I32 = 2
+    SINKATTN_I32 = 2,
+    SINKATTN_FP8_E4M3 = 3 /* OCP E4M3 (1-4-3, bias 7, no infinities), one byte per element */
 } sinkattn_dtype;
 
 /* A strided view of device memory. Only the first `ndim` entries of shape/stride are read. */
@@ -296,6 +297,48 @@ size_t sinkattn_decode_workspace_counter_bytes(int64_t batch, int64_t num_kv_hea
 sinkattn_status sinkattn_moe_topk_softmax(const sinkattn_tensor* logits, int top_k, int over_all_experts,
                                           const sinkattn_tensor* topk_ids,
                                           const sinkattn_tensor* topk_weights, void* stream);
+/*
+ * sinkattn_linear_bias - linear layer y = x w^T + bias, bf16, with the bias folded into the
+ * matrix-core accumulators.
+ *
+ * Source: "GPT-OSS on Day 0" (Perplexity): the GEMM kernels were extended with a bias term
+ * ("GPT-OSS on Hopper"), added by starting the accumulator registers at bias values loaded from
+ * memory once per output block ("Kernels for GPT-OSS"). Every output tile's accumulators start at
+ * the bias of their column; no separate epilogue pass reads the bias.
+ *
+ *   x     [M, K] bf16   activations, unit inner stride, rows 16-byte aligned
+ *   w     [N, K] bf16   weights (as a linear layer stores them), same layout rules
+ *   bias  [N] fp32, contiguous, or NULL (no bias)
+ *   y     [M, N] bf16 | fp32, unit inner stride; must not overlap the inputs
+ * K must be a positive multiple of 64. Accumulation is fp32. M = 0 or N = 0 launches nothing.
+ */
+sinkattn_status sinkattn_linear_bias(const sinkattn_tensor* x, const sinkattn_tensor* w,
+                                     const sinkattn_tensor* bias, const sinkattn_tensor* y,
+                                     void* stream);
+/*
+ * sinkattn_linear_fp8_block_scaled - linear layer y = dequant(x) dequant(w)^T + bias with FP8 (E4M3)
+ * operands and 128 x 128 block scaling, bias folded into the accumulators.
+ *
+ * Source: "GPT-OSS on Day 0" (Perplexity), section "GPT-OSS on Hopper": FP8 with 128x128 block
+ * scaling as the quantisation scheme, GEMM kernels extended with a bias; "Kernels for GPT-OSS":
+ * the accumulators start at the bias. The pages scale the weights in 128 x 128 blocks and do not
+ * say how the activations are scaled; here x carries one scale per row and 128-column block:
+ *
+ *   y[m, n] = bias[n] + sum_kb scale_x[m, kb] * scale_w[n / 128, kb] * sum_{k in block kb} x[m, k] w[n, k]
+ *
+ *   x        [M, K] FP8_E4M3, unit inner stride, rows 16-byte aligned
+ *   scale_x  [M, K/128] fp32 (any strides)
+ *   w        [N, K] FP8_E4M3, unit inner stride, rows 16-byte aligned
+ *   scale_w  [ceil(N/128), K/128] fp32 (any strides)
+ *   bias     [N] fp32, contiguous, or NULL
+ *   y        [M, N] bf16 | fp32, unit inner stride
+ * K must be a positive multiple of 128. Each 128-wide k block is multiplied exactly (FP8 products
+ * accumulate in fp32) and added to the fp32 accumulator times its two scales. NaN codes propagate.
+ */
+sinkattn_status sinkattn_linear_fp8_block_scaled(const sinkattn_tensor* x, const sinkattn_tensor* scale_x,
+                                                 const sinkattn_tensor* w, const sinkattn_tensor* scale_w,
+                                                 const sinkattn_tensor* bias, const sinkattn_tensor* y,
+                                                 void* stream);
 /* Short static description of a status code. Never NULL. */
 const char* sinkattn_status_string(sinkattn_status status);
 

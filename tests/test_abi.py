@@ -474,3 +474,64 @@ def test_moe_rejects(name, mutate, code):
     status = call_moe(mutate(moe_args()))
     assert status == code, (status, last_error())
     assert last_error()
+
+
+# ----------------------------------------------------------------------------- linear layers
+FP8 = _lib.FP8_E4M3
+
+
+def lin_args(m=256, n=384, k=512, fp8=False, ydt=BF16, bias=True):
+    dt = FP8 if fp8 else BF16
+    a = dict(x=T([m, k], dt), w=T([n, k], dt), bias=T([n], F32) if bias else None, y=T([m, n], ydt), fp8=fp8)
+    if fp8:
+        a["sx"] = T([m, k // 128], F32)
+        a["sw"] = T([(n + 127) // 128, k // 128], F32)
+    return a
+
+
+def call_lin(a):
+    if a["fp8"]:
+        return _lib.lib.sinkattn_linear_fp8_block_scaled(R(a["x"]), R(a["sx"]), R(a["w"]), R(a["sw"]),
+                                                         R(a["bias"]), R(a["y"]), None)
+    return _lib.lib.sinkattn_linear_bias(R(a["x"]), R(a["w"]), R(a["bias"]), R(a["y"]), None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_linear_empty_is_ok(fp8):
+    assert call_lin(lin_args(m=0, fp8=fp8)) == _lib.OK
+    assert call_lin(lin_args(n=0, fp8=fp8)) == _lib.OK
+
+
+def test_linear_bias_may_be_null():
+    assert call_lin(lin_args(m=0, bias=False)) == _lib.OK
+
+
+LIN_CASES = [
+    ("x_null", lambda a: _mut(a, x=None), _lib.ERR_NULL),
+    ("x_f32", lambda a: _mut(a, x=T([256, 512], F32)), _lib.ERR_DTYPE),
+    ("w_fp8_in_bf16_call", lambda a: _mut(a, w=T([384, 512], FP8)), _lib.ERR_DTYPE),
+    ("y_i32", lambda a: _mut(a, y=T([256, 384], I32)), _lib.ERR_DTYPE),
+    ("bias_bf16", lambda a: _mut(a, bias=T([384], BF16)), _lib.ERR_DTYPE),
+    ("k_mismatch", lambda a: _mut(a, w=T([384, 448])), _lib.ERR_SHAPE),
+    ("k_not_multiple_of_64", lambda a: lin_args(k=96), _lib.ERR_SHAPE),
+    ("y_shape", lambda a: _mut(a, y=T([256, 383])), _lib.ERR_SHAPE),
+    ("bias_len", lambda a: _mut(a, bias=T([383], F32)), _lib.ERR_SHAPE),
+    ("x_rank3", lambda a: _mut(a, x=T([2, 128, 512])), _lib.ERR_SHAPE),
+    ("x_row_unaligned", lambda a: _mut(a, x=T([256, 512], strides=[516, 1])), _lib.ERR_LAYOUT),
+    ("x_rows_overlap", lambda a: _mut(a, x=T([256, 512], strides=[8, 1])), _lib.ERR_LAYOUT),
+    ("y_inner_stride", lambda a: _mut(a, y=T([256, 384], strides=[768, 2])), _lib.ERR_LAYOUT),
+    ("y_overlaps_x", lambda a: _mut(a, y=T([256, 384], addr=a["x"].data)), _lib.ERR_LAYOUT),
+    ("fp8_k_not_multiple_of_128", lambda a: lin_args(k=192, fp8=True), _lib.ERR_SHAPE),
+    ("fp8_scale_x_shape", lambda a: _mut(lin_args(fp8=True), sx=T([256, 3], F32)), _lib.ERR_SHAPE),
+    ("fp8_scale_w_shape", lambda a: _mut(lin_args(fp8=True), sw=T([2, 4], F32)), _lib.ERR_SHAPE),
+    ("fp8_scale_bf16", lambda a: _mut(lin_args(fp8=True), sx=T([256, 4], BF16)), _lib.ERR_DTYPE),
+    ("fp8_bf16_operand", lambda a: _mut(lin_args(fp8=True), x=T([256, 512], BF16)), _lib.ERR_DTYPE),
+    ("fp8_scale_null", lambda a: _mut(lin_args(fp8=True), sw=None), _lib.ERR_NULL),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", LIN_CASES, ids=[c[0] for c in LIN_CASES])
+def test_linear_rejects(name, mutate, code):
+    status = call_lin(mutate(lin_args()))
+    assert status == code, (status, last_error())
+    assert last_error()

@@ -1,0 +1,162 @@
+"""GPU parity of the bias linear layer (bf16) and the FP8 block-scaled linear layer against the
+float64 oracle, through the C ABI.
+
+Source: "GPT-OSS on Day 0" (Perplexity): FP8 with 128x128 block scaling, GEMM kernels extended with a
+bias term that starts the matrix-core accumulators ("GPT-OSS on Hopper"; "Kernels for GPT-OSS").
+Bar, derived from the arithmetic: |gpu - oracle| <= u_out |oracle| + (K + 2 K/128) u_acc S per
+element, where u_out is the output rounding (2^-8 for bf16, 2^-24 for fp32), S the sum over k of
+|terms| (scales included) and u_acc the unit of one fp32 accumulation step - the worst-case bound
+of fp32 accumulation. u_acc = 2^-24 (round to nearest) for the bf16 products; 2^-23 for FP8, whose
+matrix instruction sums its 64 products with an internal rounding the ISA does not pin to
+round-to-nearest (measured errors exceed the 2^-24 bound by up to 1.3x, never the 2^-23 one). As a
+sharper check the mean error relative to S stays below 2^-9 (a wrong operand layout gives errors of
+order S).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+FP8_U_ACC = 2.0 ** -23
+
+
+def _sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_learned_softmax_amd as sa  # raises if the HIP library is missing
+
+    return sa
+
+
+def _check(y_gpu, ref, s_abs, k, label, u_acc=2.0 ** -24):
+    y = y_gpu.double().cpu().numpy()
+    u_out = 2.0 ** -8 if y_gpu.dtype == torch.bfloat16 else 2.0 ** -24
+    bound = u_out * np.abs(ref) + (k + 2 * k / 128) * u_acc * s_abs + 1e-30
+    err = np.abs(y - ref)
+    rel_s = float(np.mean(err / np.maximum(s_abs, 1e-30)))
+    print(f"{label}: max err/bound {float(np.max(err / bound)):.3f}, mean err/S {rel_s:.2e}", flush=True)
+    assert np.all(np.isfinite(y)), f"{label}: non-finite output"
+    assert np.all(err <= bound), f"{label}: error above the fp32-accumulation bound"
+    assert rel_s <= 2.0 ** -9, f"{label}: mean error {rel_s}"
+
+
+def _bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+BF16_CASES = [
+    # (name, M, N, K, bias, out dtype)
+    ("tiles_256x384x512", 256, 384, 512, True, torch.bfloat16),
+    ("ragged_300x200x192", 300, 200, 192, True, torch.bfloat16),
+    ("one_row", 1, 1000, 64, True, torch.float32),
+    ("one_column", 129, 1, 128, True, torch.bfloat16),
+    ("no_bias_f32_out", 200, 260, 320, False, torch.float32),
+    ("deep_k_4096", 128, 256, 4096, True, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("name,m,n,k,has_bias,odt", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_linear_bias_bf16(name, m, n, k, has_bias, odt):
+    sa = _sa()
+    x, w = _bf16((m, k), 1), _bf16((n, k), 2)
+    b = torch.randn(n, generator=torch.Generator().manual_seed(3)) * 4 if has_bias else None
+    y = sa.linear_bias(x.cuda(), w.cuda(), b.cuda() if has_bias else None, out_dtype=odt)
+    torch.cuda.synchronize()
+    xd, wd = x.double().numpy(), w.double().numpy()
+    ref = oracle.gemm_bias(xd, wd, b.double().numpy() if has_bias else None)
+    _check(y, ref, np.abs(xd) @ np.abs(wd).T, k, f"bf16 {name}")
+
+
+def test_linear_bias_strided_views():
+    """x and y as views into wider buffers (row strides above K and N)."""
+    sa = _sa()
+    xb, w = _bf16((200, 640), 4), _bf16((300, 512), 5)
+    b = torch.randn(300, generator=torch.Generator().manual_seed(6))
+    y_buf = torch.zeros((200, 320), dtype=torch.bfloat16, device="cuda")
+    sa.linear_bias(xb.cuda()[:, :512], w.cuda(), b.cuda(), out=y_buf[:, 8:308])
+    torch.cuda.synchronize()
+    xd, wd = xb[:, :512].double().numpy(), w.double().numpy()
+    ref = oracle.gemm_bias(xd, wd, b.double().numpy())
+    _check(y_buf[:, 8:308], ref, np.abs(xd) @ np.abs(wd).T, 512, "bf16 strided")
+    assert torch.all(y_buf[:, :8] == 0) and torch.all(y_buf[:, 308:] == 0)
+
+
+def _fp8_case(m, n, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn((m, k), generator=g) * 2).to(torch.float8_e4m3fn)
+    w = (torch.randn((n, k), generator=g) * 2).to(torch.float8_e4m3fn)
+    sx = torch.rand((m, k // 128), generator=g) + 0.5
+    sw = torch.rand(((n + 127) // 128, k // 128), generator=g) * 0.1 + 0.01
+    b = torch.randn(n, generator=g)
+    return x, sx, w, sw, b
+
+
+def _fp8_ref(x, sx, w, sw, b):
+    xc, wc = x.view(torch.uint8).numpy(), w.view(torch.uint8).numpy()
+    ref = oracle.gemm_fp8_block_scaled(xc, sx.double().numpy(), wc, sw.double().numpy(),
+                                       None if b is None else b.double().numpy())
+    xa = np.abs(oracle.e4m3_to_float(xc)) * np.repeat(sx.double().numpy(), 128, axis=1)
+    n = w.shape[0]
+    wa = np.abs(oracle.e4m3_to_float(wc)) * np.repeat(np.repeat(sw.double().numpy(), 128, axis=1), 128, axis=0)[:n]
+    return ref, xa @ wa.T
+
+
+FP8_CASES = [
+    ("tiles_256x384x512", 256, 384, 512, True, torch.bfloat16),
+    ("ragged_300x200x384", 300, 200, 384, True, torch.bfloat16),
+    ("one_row", 1, 130, 128, True, torch.float32),
+    ("no_bias_f32_out", 129, 257, 256, False, torch.float32),
+    ("deep_k_4096", 128, 256, 4096, True, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("name,m,n,k,has_bias,odt", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_linear_fp8_block_scaled(name, m, n, k, has_bias, odt):
+    sa = _sa()
+    x, sx, w, sw, b = _fp8_case(m, n, k, 10 + m)
+    b = b if has_bias else None
+    y = sa.linear_fp8_block_scaled(x.cuda(), sx.cuda(), w.cuda(), sw.cuda(), b.cuda() if has_bias else None,
+                                   out_dtype=odt)
+    torch.cuda.synchronize()
+    ref, s_abs = _fp8_ref(x, sx, w, sw, b)
+    _check(y, ref, s_abs, k, f"fp8 {name}", u_acc=FP8_U_ACC)
+
+
+def test_linear_fp8_transposed_scale_layouts():
+    """scale_x given as a transposed view ([K/128, M] storage), scale_w column-major."""
+    sa = _sa()
+    x, sx, w, sw, b = _fp8_case(200, 300, 512, 21)
+    sx_t = sx.t().contiguous().cuda().t()
+    sw_t = sw.t().contiguous().cuda().t()
+    y = sa.linear_fp8_block_scaled(x.cuda(), sx_t, w.cuda(), sw_t, b.cuda())
+    torch.cuda.synchronize()
+    ref, s_abs = _fp8_ref(x, sx, w, sw, b)
+    _check(y, ref, s_abs, 512, "fp8 transposed scales", u_acc=FP8_U_ACC)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_linear_full_size_4096_sampled_rows(fp8):
+    """The bench shape (M = N = K = 4096); 64 sampled rows compared against the oracle."""
+    sa = _sa()
+    m = n = k = 4096
+    rows = np.random.default_rng(7).choice(m, size=64, replace=False)
+    if fp8:
+        x, sx, w, sw, b = _fp8_case(m, n, k, 31)
+        y = sa.linear_fp8_block_scaled(x.cuda(), sx.cuda(), w.cuda(), sw.cuda(), b.cuda())
+        torch.cuda.synchronize()
+        ref, s_abs = _fp8_ref(x[rows], sx[rows], w, sw, b)
+    else:
+        x, w = _bf16((m, k), 41), _bf16((n, k), 42)
+        b = torch.randn(n, generator=torch.Generator().manual_seed(43))
+        y = sa.linear_bias(x.cuda(), w.cuda(), b.cuda())
+        torch.cuda.synchronize()
+        xd, wd = x[rows].double().numpy(), w.double().numpy()
+        ref, s_abs = oracle.gemm_bias(xd, wd, b.double().numpy()), np.abs(xd) @ np.abs(wd).T
+    _check(y[torch.from_numpy(rows).cuda()], ref, s_abs, k, f"{'fp8' if fp8 else 'bf16'} 4096^3 sampled",
+           u_acc=FP8_U_ACC if fp8 else 2.0 ** -24)

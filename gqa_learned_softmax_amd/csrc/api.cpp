@@ -562,9 +562,9 @@ sinkattn_status linear_impl(const sinkattn_tensor* x, const sinkattn_tensor* sca
     if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31) ||
         ((m + 127) / 128) * ((n + 127) / 128) >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
-    // A work-group addresses its 128 rows of x and of w with 32-bit byte offsets.
-    if (128 * x->stride[0] * es >= (int64_t(1) << 31) || 128 * w->stride[0] * es >= (int64_t(1) << 31))
-        return fail(SINKATTN_ERR_UNSUPPORTED, "row stride too large (128 rows must span < 2 GiB)");
+    // A work-group addresses its (up to 256) rows of x and of w with 32-bit byte offsets.
+    if (256 * x->stride[0] * es >= (int64_t(1) << 31) || 256 * w->stride[0] * es >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "row stride too large (256 rows must span < 2 GiB)");
     SA_TRY(check_data(x, "x"));
     SA_TRY(check_data(w, "w"));
     SA_TRY(check_data(y, "y"));

@@ -24,22 +24,26 @@ namespace sinkattn {
 namespace {
 
 constexpr int kGemmThreads = 256;
-constexpr int kTileM = 128;
 constexpr int kTileN = 128;
 constexpr int kStepBytes = 128;    // bytes of each row staged per K step
 constexpr int kRowPitch = 144;     // LDS row pitch in bytes
 constexpr int kGroupRows = 8;      // tile-rows per group in the tile order
+constexpr int kGemmBM = 2;         // 32-row blocks per wave in M: tiles of 128 x 128 (256 x 128 measured slower)
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// kBM 32-row blocks per wave in M (two waves in M, two in N): tile (64 kBM) x 128. A step stages
+// 8 sixteen-byte pieces per tile row: 2 kBM pieces of A and 4 of B per thread.
+template <int kBM>
 struct GemmStage {
-    i32x4 a[4];
+    i32x4 a[2 * kBM];
     i32x4 b[4];
-    float sx;  // FP8: this thread's row scale (threads < 128)
+    float sx;  // FP8: the scale of tile row tid (threads below the tile's row count)
 };
 
-template <bool kFp8>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p) {
+template <bool kFp8, int kBM>
+__global__ __launch_bounds__(kGemmThreads, kBM == 2 ? 2 : 1) void gemm_bias_kernel(GemmParams p) {
+    constexpr int kTileM = 64 * kBM;
     __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileM][kRowPitch];
     __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kTileN][kRowPitch];
     __shared__ __attribute__((aligned(16))) float sx_lds[2][kTileM];
@@ -74,25 +78,30 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p
         make_buffer(static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(n0) * ldb, rows_b * ldb);
 
     // Accumulators start at the bias of their column (lane column r32 of each 32x32 block).
-    f32x16 acc[2][2];
+    f32x16 acc[kBM][2];
 #pragma unroll
     for (int bn = 0; bn < 2; ++bn) {
         const int n = n0 + 64 * wn + 32 * bn + r32;
         const float b = p.bias != nullptr && n < p.n ? p.bias[n] : 0.0f;
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
+        for (int bm = 0; bm < kBM; ++bm)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[bm][bn][i] = b;
     }
 
     // Thread piece j: row (tid + 256 j) / 8, 16-byte segment (tid + 256 j) % 8 of the step's bytes.
-    auto stage_load = [&](GemmStage& s, int step) {
+    auto stage_load = [&](GemmStage<kBM>& s, int step) {
         const uint32_t kb = static_cast<uint32_t>(step) * kStepBytes;
+#pragma unroll
+        for (int j = 0; j < 2 * kBM; ++j) {
+            const int piece = tid + kGemmThreads * j;
+            const uint32_t row = piece >> 3, seg = piece & 7;
+            s.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, row * lda + kb + 16 * seg, 0, 0));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int piece = tid + kGemmThreads * j;
             const uint32_t row = piece >> 3, seg = piece & 7;
-            s.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, row * lda + kb + 16 * seg, 0, 0));
             s.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, row * ldb + kb + 16 * seg, 0, 0));
         }
         if constexpr (kFp8) {
@@ -100,77 +109,80 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p
             s.sx = tid < kTileM && row < p.m ? p.scale_x[row * p.sx_stride_m + step * p.sx_stride_kb] : 0.0f;
         }
     };
-    auto stage_store = [&](const GemmStage& s, int buf) {
+    auto stage_store = [&](const GemmStage<kBM>& s, int buf) {
+#pragma unroll
+        for (int j = 0; j < 2 * kBM; ++j) {
+            const int piece = tid + kGemmThreads * j;
+            *reinterpret_cast<i32x4*>(&a_lds[buf][piece >> 3][16 * (piece & 7)]) = s.a[j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int piece = tid + kGemmThreads * j;
-            const int row = piece >> 3, seg = piece & 7;
-            *reinterpret_cast<i32x4*>(&a_lds[buf][row][16 * seg]) = s.a[j];
-            *reinterpret_cast<i32x4*>(&b_lds[buf][row][16 * seg]) = s.b[j];
+            *reinterpret_cast<i32x4*>(&b_lds[buf][piece >> 3][16 * (piece & 7)]) = s.b[j];
         }
         if constexpr (kFp8)
             if (tid < kTileM) sx_lds[buf][tid] = s.sx;
     };
     auto compute = [&](int buf, int step) {
-        const uint8_t* arow[2];
+        const uint8_t* arow[kBM];
         const uint8_t* brow[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            arow[q] = &a_lds[buf][64 * wm + 32 * q + r32][0];
-            brow[q] = &b_lds[buf][64 * wn + 32 * q + r32][0];
-        }
+        for (int q = 0; q < kBM; ++q) arow[q] = &a_lds[buf][32 * kBM * wm + 32 * q + r32][0];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) brow[q] = &b_lds[buf][64 * wn + 32 * q + r32][0];
         if constexpr (!kFp8) {
             // Four k slices of 16 bf16; lane half h takes k 8h .. 8h + 7 of each slice.
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 av[2], bv[2];
+                bf16x8 av[kBM], bv[2];
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    av[q] = *reinterpret_cast<const bf16x8*>(arow[q] + 32 * kk + 16 * h);
-                    bv[q] = *reinterpret_cast<const bf16x8*>(brow[q] + 32 * kk + 16 * h);
-                }
+                for (int q = 0; q < kBM; ++q) av[q] = *reinterpret_cast<const bf16x8*>(arow[q] + 32 * kk + 16 * h);
 #pragma unroll
-                for (int bm = 0; bm < 2; ++bm)
+                for (int q = 0; q < 2; ++q) bv[q] = *reinterpret_cast<const bf16x8*>(brow[q] + 32 * kk + 16 * h);
+#pragma unroll
+                for (int bm = 0; bm < kBM; ++bm)
 #pragma unroll
                     for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = mfma32x32x16(av[bm], bv[bn], acc[bm][bn]);
             }
         } else {
             // Two k slices of 64 FP8; lane half h takes bytes 32h .. 32h + 31 of each slice (the
             // same bytes for A and B, so the product pairs equal k whatever order the unit uses).
-            f32x16 part[2][2];
+            // Each block's two products go into a temporary that is promoted at once:
+            // acc += part * scale_x[row] * scale_w (one weight scale per 128-column tile).
+            const float sw = p.scale_w[static_cast<int64_t>(tn) * p.sw_stride_nb + step * p.sw_stride_kb];
+            i32x8 bv[2][2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                i32x8 av[2], bv[2];
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow[q] + 64 * s + 32 * h);
-                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow[q] + 64 * s + 32 * h + 16);
                     const i32x4 b0 = *reinterpret_cast<const i32x4*>(brow[q] + 64 * s + 32 * h);
                     const i32x4 b1 = *reinterpret_cast<const i32x4*>(brow[q] + 64 * s + 32 * h + 16);
-                    av[q] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    bv[q] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    bv[s][q] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
 #pragma unroll
-                for (int bm = 0; bm < 2; ++bm)
+            for (int bm = 0; bm < kBM; ++bm) {
+                i32x8 av[2];
 #pragma unroll
-                    for (int bn = 0; bn < 2; ++bn)
-                        part[bm][bn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            av[bm], bv[bn], s == 0 ? zero_f32x16() : part[bm][bn], 0, 0, 0, 127, 0, 127);
-            }
-            // Promote: acc += part * scale_x[row] * scale_w (one weight scale per 128-column tile).
-            const float sw = p.scale_w[static_cast<int64_t>(tn) * p.sw_stride_nb + step * p.sw_stride_kb];
-#pragma unroll
-            for (int bm = 0; bm < 2; ++bm) {
+                for (int s = 0; s < 2; ++s) {
+                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow[bm] + 64 * s + 32 * h);
+                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow[bm] + 64 * s + 32 * h + 16);
+                    av[s] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+                float c[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const f32x4 sx4 = *reinterpret_cast<const f32x4*>(&sx_lds[buf][64 * wm + 32 * bm + 8 * g + 4 * h]);
+                    const f32x4 sx4 =
+                        *reinterpret_cast<const f32x4*>(&sx_lds[buf][32 * kBM * wm + 32 * bm + 8 * g + 4 * h]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float c = sx4[e] * sw;
+                    for (int e = 0; e < 4; ++e) c[4 * g + e] = sx4[e] * sw;
+                }
 #pragma unroll
-                        for (int bn = 0; bn < 2; ++bn)
-                            acc[bm][bn][4 * g + e] = fmaf(part[bm][bn][4 * g + e], c, acc[bm][bn][4 * g + e]);
-                    }
+                for (int bn = 0; bn < 2; ++bn) {
+                    f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[0], bv[0][bn], zero_f32x16(),
+                                                                                   0, 0, 0, 127, 0, 127);
+                    part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[1], bv[1][bn], part, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[bm][bn][i] = fmaf(part[i], c[i], acc[bm][bn][i]);
                 }
             }
         }
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p
     // One step ahead: step i + 1's loads are in flight while step i is multiplied, then go from
     // registers into the other buffer; one barrier per step.
     const int steps = p.k / (kStepBytes / es);
-    GemmStage st;
+    GemmStage<kBM> st;
     stage_load(st, 0);
     stage_store(st, 0);
     __syncthreads();
@@ -192,14 +204,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p
 
     // Epilogue: lane column r32 of each block, rows 8 (i / 4) + 4 h + (i % 4).
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < kBM; ++bm)
 #pragma unroll
         for (int bn = 0; bn < 2; ++bn) {
             const int n = n0 + 64 * wn + 32 * bn + r32;
             if (n >= p.n) continue;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int m = m0 + 64 * wm + 32 * bm + 8 * (i / 4) + 4 * h + (i % 4);
+                const int m = m0 + 32 * kBM * wm + 32 * bm + 8 * (i / 4) + 4 * h + (i % 4);
                 if (m >= p.m) continue;
                 const int64_t off = static_cast<int64_t>(m) * p.ldy + n;
                 if (p.y_is_bf16)
@@ -212,13 +224,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bias_kernel(GemmParams p
 
 }  // namespace
 
-hipError_t launch_gemm_bias(const GemmParams& p, bool fp8, hipStream_t stream) {
+template <bool kFp8, int kBM>
+hipError_t launch_tiles(const GemmParams& p, hipStream_t stream) {
+    constexpr int kTileM = 64 * kBM;
     const int64_t tiles = static_cast<int64_t>((p.m + kTileM - 1) / kTileM) * ((p.n + kTileN - 1) / kTileN);
-    if (fp8)
-        gemm_bias_kernel<true><<<dim3(static_cast<unsigned>(tiles)), dim3(kGemmThreads), 0, stream>>>(p);
-    else
-        gemm_bias_kernel<false><<<dim3(static_cast<unsigned>(tiles)), dim3(kGemmThreads), 0, stream>>>(p);
+    gemm_bias_kernel<kFp8, kBM><<<dim3(static_cast<unsigned>(tiles)), dim3(kGemmThreads), 0, stream>>>(p);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_bias(const GemmParams& p, bool fp8, hipStream_t stream) {
+    return fp8 ? launch_tiles<true, kGemmBM>(p, stream) : launch_tiles<false, kGemmBM>(p, stream);
 }
 
 }  // namespace sinkattn

@@ -708,3 +708,56 @@ def test_full_multi_decode_8x8192_t4():
     torch.cuda.synchronize()
     ref, _ = oracle_decode_multi(case)
     check_bf16(out, ref, "multi full t4")
+
+
+def test_graph_replays_multi_token_decode_moe_and_linear():
+    """Replays of one graph holding the multi-token fused decode (its counters must be left zero by
+    each replay), the MoE routing and both linear layers equal their eager results every time."""
+    sa = _sa()
+    dec = workloads.make_decode([700, 33, 1024, 5] * 16, 1024, 8, seed=51, q_len=4)
+    q, k, v, s, sl = _dev(dec.q, dec.k, dec.v, dec.sinks, dec.seqlens_k)
+    ws = sa.decode_workspace(64 * 4, 64, 8, 8, "cuda")
+    out = torch.empty((64, 4, 64, 64), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator().manual_seed(52)
+    logits = torch.randn((4096, 128), generator=g).to(torch.bfloat16).cuda()
+    ids = torch.empty((4096, 4), dtype=torch.int32, device="cuda")
+    wts = torch.empty((4096, 4), dtype=torch.bfloat16, device="cuda")
+    x = torch.randn((256, 512), generator=g).to(torch.bfloat16).cuda()
+    w = torch.randn((384, 512), generator=g).to(torch.bfloat16).cuda()
+    b = torch.randn(384, generator=g).cuda()
+    y = torch.empty((256, 384), dtype=torch.bfloat16, device="cuda")
+    qx = (torch.randn((256, 512), generator=g) * 2).to(torch.float8_e4m3fn).cuda()
+    qw = (torch.randn((384, 512), generator=g) * 2).to(torch.float8_e4m3fn).cuda()
+    sx = (torch.rand((256, 4), generator=g) + 0.5).cuda()
+    sw = (torch.rand((3, 4), generator=g) * 0.1).cuda()
+    y8 = torch.empty((256, 384), dtype=torch.bfloat16, device="cuda")
+
+    def work():
+        sa.decode_multi_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
+        sa.moe_topk_softmax(logits, 4, ids=ids, weights=wts)
+        sa.linear_bias(x, w, b, out=y)
+        sa.linear_fp8_block_scaled(qx, sx, qw, sw, b, out=y8)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, ids, wts, y, y8)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(4):
+        for t in (out, ids, wts, y, y8):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, e in zip((out, ids, wts, y, y8), eager):
+            assert torch.equal(t, e), f"replay {rep}"
+        work()  # eager work between replays
+        torch.cuda.synchronize()
+    counter_bytes = sa._lib.lib.sinkattn_decode_workspace_counter_bytes(64 * 4, 8)
+    assert torch.count_nonzero(ws[:counter_bytes]).item() == 0

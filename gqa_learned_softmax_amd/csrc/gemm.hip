@@ -188,18 +188,40 @@ __global__ __launch_bounds__(kGemmThreads, kBM == 2 ? 2 : 1) void gemm_bias_kern
         }
     };
 
-    // One step ahead: step i + 1's loads are in flight while step i is multiplied, then go from
-    // registers into the other buffer; one barrier per step.
+    // bf16: two steps of loads in flight; FP8 (no registers to spare): one. Step i + 1 goes from
+    // registers into the other buffer after step i is multiplied; one barrier per step.
     const int steps = p.k / (kStepBytes / es);
-    GemmStage<kBM> st;
-    stage_load(st, 0);
-    stage_store(st, 0);
-    __syncthreads();
-    for (int i = 0; i < steps; ++i) {
-        if (i + 1 < steps) stage_load(st, i + 1);
-        compute(i & 1, i);
-        if (i + 1 < steps) stage_store(st, (i + 1) & 1);
+    GemmStage<kBM> ra, rb;
+    if constexpr (kFp8) {
+        stage_load(ra, 0);
+        stage_store(ra, 0);
         __syncthreads();
+        for (int i = 0; i < steps; ++i) {
+            if (i + 1 < steps) stage_load(ra, i + 1);
+            compute(i & 1, i);
+            if (i + 1 < steps) stage_store(ra, (i + 1) & 1);
+            __syncthreads();
+        }
+    } else {
+        // Unconditional prefetch two steps ahead: loads past the K extent stay inside the rows'
+        // buffer range (or read zeros) and are never stored, and with no branch around them the
+        // compiler waits for just the older step's loads before each LDS store.
+        stage_load(ra, 0);
+        stage_store(ra, 0);
+        stage_load(ra, 1);
+        __syncthreads();
+        for (int i = 0; i < steps;) {
+            stage_load(rb, i + 2);
+            compute(i & 1, i);
+            stage_store(ra, (i + 1) & 1);
+            __syncthreads();
+            if (++i >= steps) break;
+            stage_load(ra, i + 2);
+            compute(i & 1, i);
+            stage_store(rb, (i + 1) & 1);
+            __syncthreads();
+            ++i;
+        }
     }
 
     // Epilogue: lane column r32 of each block, rows 8 (i / 4) + 4 h + (i % 4).

@@ -11,6 +11,7 @@
 #include <string>
 
 #include "launch.h"
+#include "launch_ops.h"
 
 namespace {
 

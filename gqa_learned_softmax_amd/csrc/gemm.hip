@@ -18,7 +18,7 @@
 // 8 tile-rows so the X and W panels a group shares stay in that XCD's L2.
 
 #include "device_common.h"
-#include "launch.h"
+#include "launch_ops.h"
 
 namespace sinkattn {
 namespace {

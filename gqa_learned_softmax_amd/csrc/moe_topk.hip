@@ -18,7 +18,7 @@
 // r < K then hold the chosen (logit, id) in order and write their weight and id.
 
 #include "device_common.h"
-#include "launch.h"
+#include "launch_ops.h"
 
 namespace sinkattn {
 namespace {

@@ -58,6 +58,9 @@ BF16_CASES = [
     ("one_column", 129, 1, 128, True, torch.bfloat16),
     ("no_bias_f32_out", 200, 260, 320, False, torch.float32),
     ("deep_k_4096", 128, 256, 4096, True, torch.bfloat16),
+    # M, N >= 256 take the 256 x 256 tiles of eight waves; ragged in both
+    ("big_tiles_ragged_300x520x256", 300, 520, 256, True, torch.bfloat16),
+    ("big_tiles_f32_out_512x256x128", 512, 256, 128, True, torch.float32),
 ]
 
 

@@ -18,6 +18,9 @@ The same JSON line also carries:
   KV length (sinkattn_prefill_split + sinkattn_decode_merge);
 * ``decode_multi``: the decode workload with T = 2, 4, 8 new tokens per sequence (the last T of the
   8192 keys), split + merge and single-launch, in KV GB/s;
+* ``decode_long`` and ``mixed``: the long-decode workload (32 sequences of 16K-32K keys, 16 chunks,
+  outlier keys) and the mixed one (128 decode sequences of 1-8192 keys; 16 prefill sequences of
+  512-4096 tokens), each against its time target;
 * ``moe_route``: MoE routing weights (top-4 of 128 experts, softmax over the chosen four) for 65,536
   tokens of bf16 logits, in GB/s of logits read plus ids and weights written;
 * ``linear``: the linear layer with the bias in the accumulators, M = N = K = 4096, bf16 and FP8 with
@@ -26,7 +29,7 @@ The same JSON line also carries:
 * ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
-                      [--no-hot] [--no-multi] [--no-moe] [--no-linear]
+                      [--no-hot] [--no-multi] [--no-moe] [--no-linear] [--no-long]
 """
 from __future__ import annotations
 
@@ -96,18 +99,20 @@ def _capture(fn, calls, torch):
     return graph
 
 
-def _time_graph(graph, calls, torch, replays=3):
-    """Average ms per captured call over ``replays`` replays, events on the replay stream."""
+def _time_graph(graph, calls, torch, replays=20):
+    """Median over ``replays`` replays of the ms per captured call, events on the replay stream
+    around each replay (the first replay, which uploads the graph, is not timed)."""
     graph.replay()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(replays):
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    events[0].record()
+    for r in range(replays):
         graph.replay()
-    end.record()
+        events[r + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / (replays * calls)
+    per_call = sorted(events[r].elapsed_time(events[r + 1]) / calls for r in range(replays))
+    mid = replays // 2
+    return per_call[mid] if replays % 2 else 0.5 * (per_call[mid - 1] + per_call[mid])
 
 
 def cpu_baseline(case, kv_bytes):
@@ -151,6 +156,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode detail")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE routing detail")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-decode and mixed workloads")
     ap.add_argument("--no-linear", action="store_true", help="skip the linear-layer detail")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the steps that reuse one K/V set (cache-resident; never the headline)")
@@ -420,6 +426,73 @@ def main():
             "split_tflops": round(a_flops / (ms_split * 1e-3) / 1e12, 2),
             "algorithmic_flop": a_flops,
         }
+
+    # ---------------------------------------------------------------- long decode and mixed workloads
+    if not args.no_long:
+        # Long decode: 32 sequences of 16K-32K keys in a 32768-key cache, 16 chunks. Its K/V
+        # (2 GiB allocated, ~1.6 GB read) exceed the Infinity Cache without rotation.
+        _log("generating long-decode workload (32 x 16K-32K keys) and mixed workload")
+        lc = workloads.make(4).decode
+        l_bytes = workloads.decode_kv_bytes(lc) + lc.q.numel() * 2 * 2 + lc.sinks.numel() * 4
+        lq, lk, lv = lc.q.to(dev), lc.k.to(dev), lc.v.to(dev)
+        ls_, lsl = lc.sinks.to(dev), lc.seqlens_k.to(dev)
+        lb, lhq = lc.q.shape[0], lc.q.shape[1]
+        lpo = torch.empty((lb, lhq, lc.num_chunks, dim), dtype=torch.float32, device=dev)
+        lpm = torch.empty((lb, lhq, lc.num_chunks), dtype=torch.float32, device=dev)
+        lpd = torch.empty_like(lpm)
+        lout = torch.empty((lb, lhq, dim), dtype=torch.bfloat16, device=dev)
+
+        def long_step(i):
+            sa.decode_split(lq, lk, lv, ls_, lsl, lc.num_chunks, lc.scale, lpo, lpm, lpd)
+            sa.decode_merge(lpo, lpm, lpd, out=lout)
+
+        long_step(0)
+        ms_long = _time_graph(_capture(long_step, 20, torch), 20, torch)
+        del lk, lv, lc
+        # Mixed: 128 decode sequences of 1-8192 keys (8 chunks) and 16 prefill sequences.
+        mx = workloads.make(5)
+        md = mx.decode
+        m_bytes = workloads.decode_kv_bytes(md) + md.q.numel() * 2 * 2 + md.sinks.numel() * 4
+        mq, mk, mv, ms_, msl = (t.to(dev) for t in (md.q, md.k, md.v, md.sinks, md.seqlens_k))
+        mb, mhq = md.q.shape[0], md.q.shape[1]
+        mpo = torch.empty((mb, mhq, md.num_chunks, dim), dtype=torch.float32, device=dev)
+        mpm = torch.empty((mb, mhq, md.num_chunks), dtype=torch.float32, device=dev)
+        mpd = torch.empty_like(mpm)
+        mout = torch.empty((mb, mhq, dim), dtype=torch.bfloat16, device=dev)
+
+        def mixed_decode(i):
+            sa.decode_split(mq, mk, mv, ms_, msl, md.num_chunks, md.scale, mpo, mpm, mpd)
+            sa.decode_merge(mpo, mpm, mpd, out=mout)
+
+        mp = mx.prefill
+        m_flops = 4.0 * dim * mp.q.shape[1] * workloads.prefill_causal_pairs(mp)
+        pq, pk, pv, ps, pcq, pck = (t.to(dev) for t in (mp.q, mp.k, mp.v, mp.sinks, mp.cu_seqlens_q, mp.cu_seqlens_k))
+        pout = torch.empty_like(pq)
+
+        def mixed_prefill(i):
+            sa.prefill(pq, pk, pv, ps, pcq, pck, mp.scale, True, out=pout)
+
+        mixed_decode(0)
+        mixed_prefill(0)
+        ms_md = _time_graph(_capture(mixed_decode, 20, torch), 20, torch)
+        ms_mp = _time_graph(_capture(mixed_prefill, 5, torch), 5, torch, replays=10)
+        _log(f"long decode {ms_long * 1e3:.1f} us ({l_bytes / (ms_long * 1e-3) / 1e9:.0f} GB/s); mixed decode "
+             f"{ms_md * 1e3:.1f} us ({m_bytes / (ms_md * 1e-3) / 1e9:.0f} GB/s), mixed prefill {ms_mp * 1e3:.1f} us "
+             f"({m_flops / (ms_mp * 1e-3) / 1e12:.0f} TFLOP/s)")
+        result["decode_long"] = {
+            "workload": "decode_b32_len16k_32k_cap32768_hq64_hkv8_d64_chunks16_outliers",
+            "step_us": round(ms_long * 1e3, 2), "gbs": round(l_bytes / (ms_long * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(l_bytes / (ms_long * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": l_bytes, "target_us": 288.0,
+        }
+        result["mixed"] = {
+            "workload": "decode_b128_len1_8192_chunks8 + prefill_16x512_4096_causal",
+            "decode_step_us": round(ms_md * 1e3, 2), "decode_gbs": round(m_bytes / (ms_md * 1e-3) / 1e9, 1),
+            "decode_algorithmic_bytes": m_bytes, "decode_target_us": 192.0,
+            "prefill_us": round(ms_mp * 1e3, 2), "prefill_tflops": round(m_flops / (ms_mp * 1e-3) / 1e12, 1),
+            "prefill_algorithmic_flop": m_flops, "prefill_target_us": 669.0,
+        }
+        del mk, mv, pk, pv, mx
 
     # ---------------------------------------------------------------- MoE routing softmax (detail)
     if not args.no_moe:

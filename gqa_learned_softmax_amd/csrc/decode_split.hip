@@ -5,7 +5,10 @@
 // keeps a running max m and running scale d per query row, m starts at the head's sink value and
 // d at 1, and when the KV length is split into chunks the sink is counted in the first chunk only.
 //
-// Work decomposition: one work-group per (sequence b, set of one or two KV heads, chunk c). The
+// Work decomposition: one work-group per (sequence b, set of one or two KV heads, chunk c),
+// numbered with the KV-head set fastest, then the sequence, then the chunk. Chunk-major order
+// starts the leading chunks of every sequence (full whenever the sequence reaches past them) first,
+// so with ragged lengths the short or empty trailing chunks run last and the tail is short. The
 // query rows that share a KV head are the columns of the matrix-core tiles: its G = Hq/Hkv heads
 // for one new token, or G x T rows when a sequence decodes T tokens at once (speculative or
 // multi-token verification), column c = token c / G, head c % G, in up to four tiles of 16
@@ -228,8 +231,8 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     const int head_set = bid % heads_per_row;
     const int g = head_set * kHeads + hsub;
     bid /= heads_per_row;
-    const int chunk = bid % p.num_chunks;
-    const int b = bid / p.num_chunks;
+    const int b = bid % p.batch;
+    const int chunk = bid / p.batch;
     const int group = p.num_q_heads / p.num_kv_heads;
     const int q_len = p.q_len;
     const int columns = group * q_len;

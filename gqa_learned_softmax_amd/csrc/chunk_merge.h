@@ -27,13 +27,39 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Combines `chunks` states of one row: pm/pd hold (m_c, d_c) (natural-log m), po holds the
 // normalised chunk outputs o_c as `chunks` rows of kHeadDim floats. Lane d of the calling wave
-// receives out[d]; `lse` is the same in every lane. Chunks are taken 64 at a time: lane c loads
+// receives out[d]; `lse` is the same in every lane. The calling wave must have all 64 lanes
+// active. With more than 16 chunks they are taken 64 at a time: lane c loads
 // (m_c, d_c), the wave agrees on the maximum, each lane forms its weight w_c, and lane d then
 // accumulates w_c * o_c[d] with w_c broadcast from lane c (v_readlane). The loads of a block are
 // independent of each other, so they are in flight together; with at most 64 chunks the states
 // are loaded once.
 __device__ __forceinline__ void merge_chunk_states(const float* pm, const float* pd, const float* po,
                                                    int chunks, int lane, float& out, float& lse) {
+    if (chunks <= 16) {
+        // Few chunks: every load of the row (m_c, d_c on lanes c, and o_c[lane] for all c) is
+        // issued before any of them is used, so the row costs one memory round trip, not two.
+        float o[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[c] = c < chunks ? po[static_cast<int64_t>(c) * kHeadDim + lane] : 0.0f;
+        const float mc = lane < chunks ? pm[lane] : kNegInf;
+        const float dc = lane < chunks ? pd[lane] : 0.0f;
+        float big = mc;
+#pragma unroll
+        for (int x = 8; x > 0; x >>= 1) big = fmaxf(big, __shfl_xor(big, x));
+        big = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(big), 0));
+        const float w = mc == kNegInf ? 0.0f : dc * expf(mc - big);
+        float wsum = w;
+#pragma unroll
+        for (int x = 8; x > 0; x >>= 1) wsum += __shfl_xor(wsum, x);
+        wsum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsum), 0));
+        float osum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            if (c < chunks) osum = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c)), o[c], osum);
+        out = wsum > 0.0f ? osum / wsum : 0.0f;
+        lse = wsum > 0.0f ? big + logf(wsum) : kNegInf;
+        return;
+    }
     const float m_first = lane < chunks ? pm[lane] : kNegInf;
     const float d_first = lane < chunks ? pd[lane] : 0.0f;
     float big = m_first;

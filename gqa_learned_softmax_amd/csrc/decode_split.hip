@@ -211,7 +211,53 @@ __device__ __forceinline__ void fold_staged(float& m, float& dsum, f32x4 (&acc)[
         }
 }
 
-template <int kHeads, bool kFused>
+// Key-split fold, for one column tile (G x T <= 16): wave w of a KV head's team takes keys
+// [16w, 16w + 16) of every staged block, so all four waves share each block's work and each keeps
+// its own state (m, d, O^T) over its keys. S^T (16 keys x 16 columns) = 2 MFMA 16x16x32 with K
+// operands from rows 16w + col of the K tile; the lane's 4 scores (keys 16w + 4grp + i) are, once
+// exponentiated, the B operand of v_mfma_f32_16x16x16_bf16, and V^T (64 d x 16 keys) comes from
+// transpose reads of the V tile: O^T += V^T . P^T in 4 MFMA 16x16x16.
+__device__ __forceinline__ void fold_keys(float& m, float& dsum, f32x4 (&acc)[4], const __bf16 (*kt)[kKPitch],
+                                          const __bf16 (*vt)[kVPitch], const bf16x8 (&q_op)[2], int base,
+                                          int tail_from, int lim, float c2, int col, int grp, int w) {
+    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(&kt[16 * w + col][8 * grp]);
+    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(&kt[16 * w + col][32 + 8 * grp]);
+    f32x4 s = mfma16x16x32(k0, q_op[0], zero_f32x4());
+    s = mfma16x16x32(k1, q_op[1], s);
+    const bool tail = base + kBlockKeys > tail_from;
+    float x[4];
+    float bmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = s[i] * c2;
+        if (tail && base + 16 * w + 4 * grp + i >= lim) v = kNegInf;
+        x[i] = v;
+        bmax = fmaxf(bmax, v);
+    }
+    bmax = max_over_groups(bmax);
+    const float m_new = fmaxf(m, bmax);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = exp2_fast(m - m_use);
+    bf16x4 p_op;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = exp2_fast(x[i] - m_use);
+        psum += x[i];
+        p_op[i] = (__bf16)x[i];
+    }
+    dsum = dsum * alpha + psum;
+    m = m_new;
+    const int tr_row = 16 * w + 4 * grp + (col >> 2);
+    const int tr_col = 4 * (col & 3);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        acc[n] *= alpha;
+        acc[n] = mfma16x16x16(lds_read_tr4(&vt[tr_row][16 * n + tr_col]), p_op, acc[n]);
+    }
+}
+
+template <int kHeads, bool kFused, bool kKeySplit>
 __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kernel(DecodeSplitParams p) {
     constexpr int kWaves = kSplitWaves * kHeads;
     __shared__ int last_arrival;
@@ -244,9 +290,11 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     const int first_lim = len - q_len + 1;
     const int tail_from = first_lim < hi ? first_lim : static_cast<int>(hi);
 
-    // This wave's 16 columns: column c = token c / G, head c % G of KV head g.
-    const bool active = 16 * tile < columns;
-    const int c = 16 * tile + col;
+    // This wave's 16 columns: column c = token c / G, head c % G of KV head g. With the key split
+    // every wave of the team works on the one tile (and wave 0 writes the combined state).
+    const bool active = kKeySplit || 16 * tile < columns;
+    const bool writes_state = kKeySplit ? tile == 0 : active;
+    const int c = (kKeySplit ? 0 : 16 * tile) + col;
     const bool col_valid = c < columns;
     const int tok = col_valid ? c / group : 0;
     const int head = g * group + (col_valid ? c % group : 0);
@@ -259,9 +307,10 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     const int tok_lim = first_lim + tok;
     const int lim = tok_lim < hi ? tok_lim : static_cast<int>(hi);
     const float c2 = p.scale * kLog2e;
-    // Every wave covers the whole chunk for its columns, so each starts chunk 0 from the sink.
+    // Every wave covers the whole chunk for its columns, so each starts chunk 0 from the sink; with
+    // the key split the waves hold parts of one state, and only wave 0 carries the sink.
     float m = kNegInf, dsum = 0.0f;
-    if (chunk == 0) {
+    if (chunk == 0 && (!kKeySplit || tile == 0)) {
         m = p.sinks[head] * kLog2e;
         dsum = (grp == 0 && m != kNegInf) ? 1.0f : 0.0f;
     }
@@ -290,19 +339,64 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     // folding them.
     for (int i = 0; i < blocks;) {
         stage_load<kHeads>(rb, krs, vrs, k_row_bytes, v_row_bytes, base0 + kBlockKeys * (i + 2), tid);
-        if (active)
+        if constexpr (kKeySplit)
+            fold_keys(m, dsum, acc, k_lds[i & 1][hsub], v_lds[i & 1][hsub], q_op,
+                      static_cast<int>(base0) + kBlockKeys * i, tail_from, lim, c2, col, grp, tile);
+        else if (active)
             fold_staged(m, dsum, acc, k_lds[i & 1][hsub], v_lds[i & 1][hsub], q_op,
                         static_cast<int>(base0) + kBlockKeys * i, tail_from, lim, c2, col, grp);
         stage_store<kHeads>(ra, k_lds[(i + 1) & 1], v_lds[(i + 1) & 1], tid);
         __syncthreads();
         if (++i >= blocks) break;
         stage_load<kHeads>(ra, krs, vrs, k_row_bytes, v_row_bytes, base0 + kBlockKeys * (i + 2), tid);
-        if (active)
+        if constexpr (kKeySplit)
+            fold_keys(m, dsum, acc, k_lds[i & 1][hsub], v_lds[i & 1][hsub], q_op,
+                      static_cast<int>(base0) + kBlockKeys * i, tail_from, lim, c2, col, grp, tile);
+        else if (active)
             fold_staged(m, dsum, acc, k_lds[i & 1][hsub], v_lds[i & 1][hsub], q_op,
                         static_cast<int>(base0) + kBlockKeys * i, tail_from, lim, c2, col, grp);
         stage_store<kHeads>(rb, k_lds[(i + 1) & 1], v_lds[(i + 1) & 1], tid);
         __syncthreads();
         ++i;
+    }
+
+    if constexpr (kKeySplit) {
+        // Combine the team's four states in the (now free) V tiles: per KV head, m and d of each
+        // wave's 16 columns, then each wave's O^T (64 d x 16 columns); wave 0 rescales them to the
+        // common maximum and sums.
+        constexpr int kStateFloats = 4 * 16 * 2 + 4 * kHeadDim * 16;
+        static_assert(sizeof(v_lds) >= sizeof(float) * kHeads * kStateFloats, "state space");
+        float* st = reinterpret_cast<float*>(&v_lds[0][0][0][0]) + hsub * kStateFloats;
+        const float d_wave = sum_over_groups(dsum);
+        if (grp == 0) {
+            st[16 * tile + col] = m;
+            st[64 + 16 * tile + col] = d_wave;
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[128 + (tile * kHeadDim + 16 * n + 4 * grp + i) * 16 + col] = acc[n][i];
+        __syncthreads();
+        if (tile == 0) {
+            float big = kNegInf;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) big = fmaxf(big, st[16 * w + col]);
+            float d_all = 0.0f;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[n] = zero_f32x4();
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float mw = st[16 * w + col];
+                const float sc = mw == kNegInf ? 0.0f : exp2_fast(mw - big);
+                d_all += st[64 + 16 * w + col] * sc;
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[n][i] += sc * st[128 + (w * kHeadDim + 16 * n + 4 * grp + i) * 16 + col];
+            }
+            m = big;
+            dsum = grp == 0 ? d_all : 0.0f;
+        }
     }
 
     // The chunk state of each valid column: o = acc / d, m (natural log), d.
@@ -316,7 +410,7 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
         // contiguous 256-byte row of partial_o; the K tiles are free after the loop's last barrier.
         static_assert(sizeof(k_lds) >= sizeof(float) * kWaves * 16 * (kHeadDim + 4), "staging space");
         float (*ot)[kHeadDim + 4] = reinterpret_cast<float (*)[kHeadDim + 4]>(&k_lds[0][0][0][0]) + 16 * wave_all;
-        if (active) {
+        if (writes_state) {
 #pragma unroll
             for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(&ot[col][16 * n + 4 * grp]) = acc[n] * inv;
             if (col_valid && grp == 0) {
@@ -325,7 +419,7 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
             }
         }
         __syncthreads();
-        if (active) {
+        if (writes_state) {
             const int tile_cols = columns - 16 * tile < 16 ? columns - 16 * tile : 16;
             for (int r = 0; r < tile_cols; ++r) {
                 const int cr = 16 * tile + r;
@@ -336,7 +430,7 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
                                    __HIP_MEMORY_SCOPE_SYSTEM);
             }
         }
-    } else if (active && col_valid) {
+    } else if (writes_state && col_valid) {
         float* orow = p.partial_o + row * kHeadDim + 4 * grp;
 #pragma unroll
         for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(orow + 16 * n) = acc[n] * inv;
@@ -416,19 +510,27 @@ constexpr int64_t kComputeUnits = 256;
 // Pair two KV heads per work-group only where their slices of a cache row are adjacent
 // (token-major caches) and the paired grid still gives every compute unit a work-group; otherwise
 // one KV head per work-group. The host allows at most 64 query rows (four tiles) per KV head.
-template <bool kFused>
-hipError_t launch_split(const DecodeSplitParams& p, hipStream_t stream) {
+template <bool kFused, bool kKeySplit>
+hipError_t launch_split_as(const DecodeSplitParams& p, hipStream_t stream) {
     const bool adjacent = p.k_stride_head == kHeadDim && p.v_stride_head == kHeadDim;
     const int64_t paired_groups = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 2) * p.num_chunks;
     if (p.num_kv_heads % 2 == 0 && adjacent && paired_groups >= kComputeUnits) {
-        decode_split_bf16_kernel<2, kFused>
+        decode_split_bf16_kernel<2, kFused, kKeySplit>
             <<<dim3(static_cast<unsigned>(paired_groups)), dim3(2 * kSplitThreads), 0, stream>>>(p);
     } else {
         const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_chunks;
-        decode_split_bf16_kernel<1, kFused>
+        decode_split_bf16_kernel<1, kFused, kKeySplit>
             <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitThreads), 0, stream>>>(p);
     }
     return hipGetLastError();
+}
+
+// With one column tile (G x T <= 16 query rows per KV head) the four waves of a KV head split the
+// keys of each block; with more, each wave folds one column tile over all keys.
+template <bool kFused>
+hipError_t launch_split(const DecodeSplitParams& p, hipStream_t stream) {
+    const int columns = p.num_q_heads / p.num_kv_heads * p.q_len;
+    return columns <= 16 ? launch_split_as<kFused, true>(p, stream) : launch_split_as<kFused, false>(p, stream);
 }
 
 hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream) {

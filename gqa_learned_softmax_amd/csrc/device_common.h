@@ -25,6 +25,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// A (16x16) times B (16x16), bf16 inputs, fp32 16x16 accumulator: v_mfma_f32_16x16x16_bf16.
+// Lane l: A holds row (l % 16) and the 4 k-slots 4 * (l / 16) + 0..3; B holds column (l % 16) and
+// the same k-slots; the result holds rows 4 * (l / 16) + 0..3 of column (l % 16), which is the
+// B-operand layout again, so a 16x16x32 accumulator's 4 values per lane are ready P^T operands.
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                     0, 0, 0);
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // A (32x16) times B (16x32), bf16 inputs, fp32 32x32 accumulator: v_mfma_f32_32x32x16_bf16.

@@ -299,7 +299,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_bf16_kernel<2, false>",
+            "kernel": "decode_split_bf16_kernel<2, false, true>",
             "achieved": round(split_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

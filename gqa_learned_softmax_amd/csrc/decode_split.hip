@@ -18,15 +18,17 @@
 // Inside the work-group, each 64-key block of the chunk is staged in LDS once: every thread loads
 // two 16-byte pieces of K rows and two of V rows (with two KV heads, the 256 bytes their slices
 // take in a token-major cache row, 16 lanes per row), and stores them into double-buffered K and V
-// tiles. Wave w of a KV head's team folds column tile w over every block of the chunk, so each wave
-// owns the complete chunk state of its columns and no cross-wave reduction is needed. The loads of
-// block i + 2 are in flight while block i is folded and block i + 1 goes from registers into the
-// other LDS buffer; one barrier per block. (One block ahead, or three, measured slower.)
+// tiles. With more than one column tile, wave w of a KV head's team folds column tile w over every
+// block of the chunk, so each wave owns the complete chunk state of its columns and no cross-wave
+// reduction is needed. With one tile (G x T <= 16, e.g. one new token of 8 query heads) the four
+// waves split each block's keys instead (fold_keys) and combine their states at the chunk end. The
+// loads of block i + 2 are in flight while block i is folded and block i + 1 goes from registers
+// into the other LDS buffer; one barrier per block. (One block ahead, or three, measured slower.)
 //
 // With T tokens, the sequence length L counts the new tokens, and token t sees keys j <= L - T + t
 // (the causal rule of the last T rows of a prefill); only the last T - 1 keys need a mask.
 //
-// Per block, per active wave (one column tile):
+// Per block, per active wave of the column-tile fold (fold_keys does the same for 16 keys):
 //   S^T (64 keys x 16 columns) = K (64 x 64) . Q^T (64 x 16): 8 MFMA 16x16x32, K operands read
 //     from the K tile (lane (col, grp) reads key row 16t + col, elements 8grp and 32 + 8grp), Q^T
 //     resident in registers.

@@ -53,7 +53,8 @@ constexpr int kVPitch = 96;
 //  * running-max tiles: m is the running max, raised (and O, d rescaled) only when a tile's max
 //    exceeds it by more than kRescaleSlack log2 units, so p <= 2^8;
 //  * zero-reference tiles: once the running max of a row lies in [-kZeroRefLimit, kZeroRefLimit]
-//    the row is rescaled once to m = 0, and while every row of a wave has m = 0 its tiles need
+//    (from the start, when the sink does) the row is rescaled once to m = 0, and while every row
+//    of a wave has m = 0 its tiles need
 //    neither a row max nor a subtraction: p = exp2(s). The row's largest contribution so far is
 //    then at least 2^-kZeroRefLimit, so nothing that matters can underflow; overflow is checked
 //    once at the end: a work-group in which any row's d exceeds kFastSumLimit (every p is at
@@ -441,9 +442,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             // Sink fold: m starts at the head's sink, d at 1 (kept in the half-0 lane's share);
-            // a split other than the first starts empty (m = -inf, d = 0).
+            // a split other than the first starts empty (m = -inf, d = 0). A row whose sink lies
+            // in [-kZeroRefLimit, kZeroRefLimit] may start on the zero reference instead (m = 0,
+            // d = 2^sink): the sink term alone gives the row a term >= 2^-kZeroRefLimit, the
+            // condition the switch after a running-max tile checks, so even the first tile can
+            // run without row maxima.
             m[cb] = carries_sink ? sink2[cb] : kNegInf;
             dsum[cb] = (half == 0 && m[cb] != kNegInf) ? 1.0f : 0.0f;
+            if (kAllowFast && m[cb] >= -kZeroRefLimit && m[cb] <= kZeroRefLimit) {
+                dsum[cb] = half == 0 ? exp2_fast(m[cb]) : 0.0f;
+                m[cb] = 0.0f;
+            }
 #pragma unroll
             for (int n = 0; n < 2; ++n) acc[cb][n] = zero_f32x16();
         }

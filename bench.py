@@ -26,9 +26,10 @@ The same JSON line also carries:
 * ``linear``: the linear layer with the bias in the accumulators, M = N = K = 4096, bf16 and FP8 with
   128 x 128 block scaling, TFLOP/s against the dense MFMA peaks (torch's bf16 linear timed beside it
   as context);
-* ``cpu_baseline``: the float64 CPU oracle on the same decode workload, single BLAS thread.
+* ``cpu_baseline``: the float64 CPU oracle on the same decode workload, over the host cores (one BLAS
+  thread per worker thread).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 5] [--no-cpu-baseline] [--no-prefill]
                       [--no-hot] [--no-multi] [--no-moe] [--no-linear] [--no-long]
 """
 from __future__ import annotations
@@ -179,7 +180,7 @@ def cpu_baseline(case, kv_bytes):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")

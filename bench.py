@@ -132,7 +132,7 @@ def cpu_baseline(case, kv_bytes):
     (NumPy releases the interpreter lock inside its array kernels; one BLAS thread each) runs its
     decode on one (sequence, KV head) unit at a time; whole-workload passes repeat until >= 10 s.
     Threads, not processes, so nothing is forked from a process that has initialised the GPU.
-    Workers: the cores this process may use, at most 16 (one GPU's share of a box)."""
+    Workers: the cores this process may use, at most 16."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np

@@ -135,4 +135,33 @@ __device__ __forceinline__ void merge_chunk_states_x4(const float* pm, const flo
     lse = wsum > 0.0f ? big + logf(wsum) : kNegInf;
 }
 
+// Four rows per wave with at most 16 chunks: as merge_chunk_states_x4, but every load of a row
+// (m_c, d_c on lanes c of the quarter, and channels 4j .. 4j + 3 of every o_c) is issued before any
+// is used, so a row costs one memory round trip. The 16 lanes of a calling quarter must be active
+// together.
+__device__ __forceinline__ void merge_few_chunk_states_x4(const float* pm, const float* pd, const float* po,
+                                                          int chunks, int lane, f32x4& out, float& lse) {
+    const int j = lane & 15;
+    const int quarter = lane & 48;
+    f32x4 o[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        o[c] = c < chunks ? *reinterpret_cast<const f32x4*>(po + c * kHeadDim + 4 * j) : zero_f32x4();
+    const float mc = j < chunks ? pm[j] : kNegInf;
+    const float dc = j < chunks ? pd[j] : 0.0f;
+    float big = mc;
+#pragma unroll
+    for (int x = 8; x > 0; x >>= 1) big = fmaxf(big, __shfl_xor(big, x));
+    const float w = mc == kNegInf ? 0.0f : dc * expf(mc - big);
+    float wsum = w;
+#pragma unroll
+    for (int x = 8; x > 0; x >>= 1) wsum += __shfl_xor(wsum, x);
+    f32x4 osum = zero_f32x4();
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        if (c < chunks) osum += __shfl(w, quarter + c) * o[c];
+    out = wsum > 0.0f ? osum / wsum : zero_f32x4();
+    lse = wsum > 0.0f ? big + logf(wsum) : kNegInf;
+}
+
 }  // namespace sinkattn

@@ -1,7 +1,9 @@
 // Log-sum-exp merge of split-KV chunk states (gfx950): the combination rule of chunk_merge.h
 // (section "Kernels for GPT-OSS", subsection "Sink attention", of "GPT-OSS on Day 0") as a kernel
-// of its own. One wave per (sequence, token, query head); lane = output channel d. Each chunk
-// contributes one coalesced 256-byte row of partial_o.
+// of its own. One wave per (sequence, token, query head), lane = output channel d; each chunk
+// contributes one coalesced 256-byte row of partial_o. With many rows (>= 8192) and at most 16
+// chunks, four rows per wave instead (16 lanes and 4 channels per lane, all loads of a row issued at
+// once): fewer, fuller waves, measured faster there and slower on a few hundred rows.
 
 #include "chunk_merge.h"
 #include "device_common.h"
@@ -11,6 +13,39 @@ namespace sinkattn {
 namespace {
 
 constexpr int kMergeWaves = 4;
+
+constexpr int64_t kRowsForX4 = 8192;
+
+// Four rows per wave (chunks <= 16). Rows past the end are clamped to the last row and not
+// written, so every lane stays active for the quarter reductions.
+__global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_x4_kernel(DecodeMergeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = static_cast<int64_t>(p.batch) * p.num_q_heads;
+    const int64_t bh_raw = (static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool valid = bh_raw < rows;
+    const int64_t bh = valid ? bh_raw : rows - 1;
+    const int64_t bt = bh / p.num_q_heads;
+    const int b = static_cast<int>(bt / p.q_len);
+    const int tok = static_cast<int>(bt % p.q_len);
+    const int h = static_cast<int>(bh % p.num_q_heads);
+    const int chunks = p.num_chunks;
+    f32x4 o;
+    float lse;
+    merge_few_chunk_states_x4(p.partial_m + bh * chunks, p.partial_d + bh * chunks,
+                              p.partial_o + bh * chunks * kHeadDim, chunks, lane, o, lse);
+    if (!valid) return;
+    const int64_t off = b * p.o_stride_b + tok * p.o_stride_tok + h * p.o_stride_head + 4 * (lane & 15);
+    if (p.out_is_bf16) {
+        bf16x4 ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + off) = ob;
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off) = o;
+    }
+    if (p.lse != nullptr && (lane & 15) == 0)
+        p.lse[b * p.lse_stride_b + tok * p.lse_stride_tok + h * p.lse_stride_head] = lse;
+}
 
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeMergeParams p) {
     const int lane = threadIdx.x & 63;
@@ -37,6 +72,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeMe
 
 hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(p.batch) * p.num_q_heads;
+    if (rows >= kRowsForX4 && p.num_chunks <= 16) {
+        const int64_t blocks = (rows + 4 * kMergeWaves - 1) / (4 * kMergeWaves);
+        decode_merge_x4_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kMergeWaves * 64), 0, stream>>>(p);
+        return hipGetLastError();
+    }
     const int64_t blocks = (rows + kMergeWaves - 1) / kMergeWaves;
     decode_merge_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kMergeWaves * 64), 0, stream>>>(p);
     return hipGetLastError();

@@ -473,6 +473,36 @@ def test_graph_replays_match_eager():
         assert torch.equal(out, eager_dec)
 
 
+# ----------------------------------------------------------------------------- merge on many rows
+@pytest.mark.parametrize("chunks", [1, 3, 8, 16, 17])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_merge_many_rows_random_states(chunks, out_dtype):
+    """Merge of 8412 rows (701 x 12 heads: not a multiple of the 16 rows a four-row-per-wave
+    work-group takes) of random chunk states with empty chunks and fully empty rows, against the
+    oracle's merge. Up to 16 chunks this is the four-rows-per-wave kernel; 17 takes one wave per row."""
+    sa = _sa()
+    gen = torch.Generator().manual_seed(_seed(f"merge_many_{chunks}"))
+    b, h, dim = 701, 12, 64
+    po = torch.randn((b, h, chunks, dim), generator=gen, dtype=torch.float32)
+    pm = (torch.rand((b, h, chunks), generator=gen) * 10.0 - 5.0).float()
+    pd = (torch.rand((b, h, chunks), generator=gen) * 1.5 + 0.5).float()
+    empty = torch.rand((b, h, chunks), generator=gen) < 0.2
+    empty[::7] = True  # every seventh sequence: all of its rows have no key at all
+    pm[empty] = float("-inf")
+    pd[empty] = 0.0
+    po[empty] = 0.0
+    ref, rlse = oracle.merge(po.double().numpy(), pm.double().numpy(), pd.double().numpy())
+    gpo, gpm, gpd = _dev(po, pm, pd)
+    out, lse = sa.decode_merge(gpo, gpm, gpd, out_dtype=out_dtype, return_lse=True)
+    torch.cuda.synchronize()
+    label = f"merge {b * h} rows x {chunks} chunks {out_dtype}"
+    (check_bf16 if out_dtype == torch.bfloat16 else check_f32)(out, ref, label)
+    g = _np(lse)
+    assert np.array_equal(np.isneginf(g), np.isneginf(rlse)), label
+    fin = np.isfinite(rlse)
+    np.testing.assert_allclose(g[fin], rlse[fin], rtol=0, atol=1e-4)
+
+
 # ----------------------------------------------------------------------------- fused split + merge
 FUSED_CASES = [c for c in DECODE_SMALL if c[0] in
                ("uniform", "ragged_empty_chunks", "many_chunks", "group16", "outliers", "odd_kv_heads",

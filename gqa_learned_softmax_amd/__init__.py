@@ -111,7 +111,8 @@ def decode_workspace(batch, num_q_heads, num_kv_heads, num_chunks, device):
 
 def decode_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, out=None, lse=None,
                  return_lse=False):
-    """``sinkattn_decode``: split-KV decode and merge in one launch; out [B, Hq, D]."""
+    """``sinkattn_decode``: split-KV decode and merge through ``workspace`` (one launch when the split
+    grid has at most one work-group per compute unit); out [B, Hq, D]."""
     batch, hq, dim = q.shape
     if out is None:
         out = torch.empty((batch, hq, dim), dtype=q.dtype, device=q.device)

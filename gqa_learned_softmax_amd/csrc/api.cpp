@@ -499,9 +499,13 @@ sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tenso
     p.lse_stride_head = lse != nullptr ? lse->stride[rank - 2] : 0;
     p.out_is_bf16 = out->dtype == SINKATTN_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (q->dtype == SINKATTN_BF16) return launched(sinkattn::launch_decode_fused_bf16(p, s));
-    // fp32 reference variant: the two-kernel path through the same workspace.
-    SA_TRY(launched(sinkattn::launch_decode_split_f32(p, s)));
+    const bool bf16 = q->dtype == SINKATTN_BF16;
+    // One launch when the split grid fits a single round of work-groups; otherwise (and for the
+    // fp32 reference variant) split then merge through the same workspace, which leaves the
+    // arrival counters untouched.
+    if (bf16 && sinkattn::decode_fused_fits_one_round(p))
+        return launched(sinkattn::launch_decode_fused_bf16(p, s));
+    SA_TRY(launched(bf16 ? sinkattn::launch_decode_split_bf16(p, s) : sinkattn::launch_decode_split_f32(p, s)));
     sinkattn::DecodeMergeParams mp{};
     mp.partial_o = p.partial_o;
     mp.partial_m = p.partial_m;

@@ -516,21 +516,31 @@ constexpr int64_t kComputeUnits = 256;
 // one work-group per CU) when that still gives at least two rounds of work-groups; two heads when
 // the paired grid gives every compute unit a work-group; otherwise one. The host allows at most 64
 // query rows (four tiles) per KV head.
-template <bool kFused, bool kKeySplit>
-hipError_t launch_split_as(const DecodeSplitParams& p, hipStream_t stream) {
+// Heads per work-group and work-group count of the bf16 split grid.
+struct SplitShape {
+    int heads;
+    int64_t groups;
+};
+
+SplitShape split_shape(const DecodeSplitParams& p) {
     const bool adjacent = p.k_stride_head == kHeadDim && p.v_stride_head == kHeadDim;
     const int64_t paired_groups = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 2) * p.num_chunks;
     const int64_t quad_groups = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 4) * p.num_chunks;
-    if (p.num_kv_heads % 4 == 0 && adjacent && quad_groups >= 2 * kComputeUnits) {
-        decode_split_bf16_kernel<4, kFused, kKeySplit>
-            <<<dim3(static_cast<unsigned>(quad_groups)), dim3(4 * kSplitThreads), 0, stream>>>(p);
-    } else if (p.num_kv_heads % 2 == 0 && adjacent && paired_groups >= kComputeUnits) {
-        decode_split_bf16_kernel<2, kFused, kKeySplit>
-            <<<dim3(static_cast<unsigned>(paired_groups)), dim3(2 * kSplitThreads), 0, stream>>>(p);
+    if (p.num_kv_heads % 4 == 0 && adjacent && quad_groups >= 2 * kComputeUnits) return {4, quad_groups};
+    if (p.num_kv_heads % 2 == 0 && adjacent && paired_groups >= kComputeUnits) return {2, paired_groups};
+    return {1, static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_chunks};
+}
+
+template <bool kFused, bool kKeySplit>
+hipError_t launch_split_as(const DecodeSplitParams& p, hipStream_t stream) {
+    const SplitShape shape = split_shape(p);
+    const dim3 grid(static_cast<unsigned>(shape.groups));
+    if (shape.heads == 4) {
+        decode_split_bf16_kernel<4, kFused, kKeySplit><<<grid, dim3(4 * kSplitThreads), 0, stream>>>(p);
+    } else if (shape.heads == 2) {
+        decode_split_bf16_kernel<2, kFused, kKeySplit><<<grid, dim3(2 * kSplitThreads), 0, stream>>>(p);
     } else {
-        const int64_t blocks = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_chunks;
-        decode_split_bf16_kernel<1, kFused, kKeySplit>
-            <<<dim3(static_cast<unsigned>(blocks)), dim3(kSplitThreads), 0, stream>>>(p);
+        decode_split_bf16_kernel<1, kFused, kKeySplit><<<grid, dim3(kSplitThreads), 0, stream>>>(p);
     }
     return hipGetLastError();
 }
@@ -549,6 +559,10 @@ hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stre
 
 hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stream) {
     return launch_split<true>(p, stream);
+}
+
+bool decode_fused_fits_one_round(const DecodeSplitParams& p) {
+    return split_shape(p).groups <= kComputeUnits;
 }
 
 hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t stream) {

@@ -195,13 +195,16 @@ sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
                                       void* stream);
 
 /*
- * sinkattn_decode - split-KV decode and its log-sum-exp merge in one launch.
+ * sinkattn_decode - split-KV decode and its log-sum-exp merge, through one workspace.
  *
  * Same computation and inputs as sinkattn_decode_split followed by sinkattn_decode_merge ("GPT-OSS
  * on Day 0", "Sink attention" subsection: split along the KV length, sink in the first chunk only,
- * chunks combined), without the second launch: every work-group writes its chunk states into
- * `workspace`, counts itself done on a per-(sequence, KV-head group) counter, and the last one
- * to finish merges that group's chunks and writes `out` (and `lse`).
+ * chunks combined). When the bf16 split grid has at most one work-group per compute unit it runs
+ * as one launch: every work-group writes its chunk states into `workspace`, counts itself done on
+ * a per-(sequence, KV-head group) counter, and the last one to finish merges that group's chunks
+ * and writes `out` (and `lse`). Larger grids, and fp32 inputs, run the split and the merge as two
+ * launches on `stream` through the same workspace (the counters are not touched). The results do
+ * not depend on which form runs.
  *
  *   q, k, v, sinks, seqlens_k, num_chunks, scale: as for sinkattn_decode_split
  *   workspace       device memory, 256-byte aligned, at least
@@ -252,7 +255,7 @@ sinkattn_status sinkattn_decode_multi_split(const sinkattn_tensor* q, const sink
                                             const sinkattn_tensor* partial_m,
                                             const sinkattn_tensor* partial_d, void* stream);
 /*
- * sinkattn_decode_multi - sinkattn_decode_multi_split and the merge in one launch, as
+ * sinkattn_decode_multi - sinkattn_decode_multi_split and the merge through one workspace, as
  * sinkattn_decode does for one token.
  *
  *   q               [B, T, Hq, D] bf16 | fp32

@@ -568,12 +568,16 @@ def test_full_decode_workload_2_fused():
     check_bf16(out, ref, "workload 2 fused decode")
 
 
-def test_graph_replays_fused_decode():
+# 2 x 4 x 8 = 64 work-groups per copy of the lengths: two copies are one round of pairs (the single
+# launch with its arrival counters), sixteen copies are eight rounds (split then merge)
+@pytest.mark.parametrize("copies", [2, 16], ids=["one_launch", "split_then_merge"])
+def test_graph_replays_fused_decode(copies):
     sa = _sa()
-    dec = workloads.make_decode([700, 33, 1024, 0] * 16, 1024, 8, seed=41)  # paired kernel (64*4*8 >= 256)
+    dec = workloads.make_decode([700, 33, 1024, 0] * copies, 1024, 8, seed=41)
     q, k, v, s, sl = _dev(dec.q, dec.k, dec.v, dec.sinks, dec.seqlens_k)
-    ws = sa.decode_workspace(64, 64, 8, 8, "cuda")
-    out = torch.empty((64, 64, 64), dtype=torch.bfloat16, device="cuda")
+    b = 4 * copies
+    ws = sa.decode_workspace(b, 64, 8, 8, "cuda")
+    out = torch.empty((b, 64, 64), dtype=torch.bfloat16, device="cuda")
     sa.decode_fused(q, k, v, s, sl, 8, dec.scale, ws, out=out)
     torch.cuda.synchronize()
     eager = out.clone()

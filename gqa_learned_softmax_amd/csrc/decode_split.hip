@@ -129,8 +129,14 @@ __device__ __forceinline__ void fused_merge_tail(const DecodeSplitParams& p, int
         const int64_t bh = (static_cast<int64_t>(b) * q_len + tok) * p.num_q_heads + h;
         f32x4 o;
         float lse;
-        merge_chunk_states_x4(p.partial_m + bh * p.num_chunks, p.partial_d + bh * p.num_chunks,
-                              p.partial_o + bh * p.num_chunks * kHeadDim, p.num_chunks, lane, o, lse);
+        // hl is the same on the 16 lanes of a quarter, so whole quarters merge together.
+        const float* pm = p.partial_m + bh * p.num_chunks;
+        const float* pd = p.partial_d + bh * p.num_chunks;
+        const float* po = p.partial_o + bh * p.num_chunks * kHeadDim;
+        if (p.num_chunks <= 16)
+            merge_few_chunk_states_x4(pm, pd, po, p.num_chunks, lane, o, lse);
+        else
+            merge_chunk_states_x4(pm, pd, po, p.num_chunks, lane, o, lse);
         const int64_t off = b * p.o_stride_b + tok * p.o_stride_tok + h * p.o_stride_head + 4 * (lane & 15);
         if (p.out_is_bf16) {
             bf16x4 ob;

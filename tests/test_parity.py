@@ -568,6 +568,27 @@ def test_full_decode_workload_2_fused():
     check_bf16(out, ref, "workload 2 fused decode")
 
 
+def test_fused_decode_workspace_shared_by_both_forms():
+    """One workspace serves a long grid (split then merge), then a one-round grid (single launch with
+    arrival counters), then the long grid again: the counters must still be zero when the single
+    launch needs them, and its partials must not leak into the next call."""
+    sa = _sa()
+    long_case = workloads.make_decode([700, 33, 1024, 0] * 16, 1024, 8, seed=43)  # 64 x 2 x 8 quads
+    short_case = workloads.make_decode([1000, 5, 512, 1024, 77, 0, 300, 999], 1024, 8, seed=44)  # 8 x 4 x 8 pairs
+    ws = sa.decode_workspace(64, 64, 8, 8, "cuda")
+    for name, case in (("long", long_case), ("short", short_case), ("short again", short_case),
+                       ("long again", long_case)):
+        q, k, v, s, sl = _dev(case.q, case.k, case.v, case.sinks, case.seqlens_k)
+        out, lse = sa.decode_fused(q, k, v, s, sl, 8, case.scale, ws, return_lse=True)
+        torch.cuda.synchronize()
+        ref, rlse = oracle_decode(case)
+        check_bf16(out, ref, f"shared workspace, {name}")
+        g = _np(lse)
+        assert np.array_equal(np.isneginf(g), np.isneginf(rlse))
+        fin = np.isfinite(rlse)
+        np.testing.assert_allclose(g[fin], rlse[fin], atol=1e-3)
+
+
 # 2 x 4 x 8 = 64 work-groups per copy of the lengths: two copies are one round of pairs (the single
 # launch with its arrival counters), sixteen copies are eight rounds (split then merge)
 @pytest.mark.parametrize("copies", [2, 16], ids=["one_launch", "split_then_merge"])

@@ -210,7 +210,11 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
         __syncthreads();
         for (int i = 0; i < steps; ++i) {
             if (i + 1 < steps) stage_load(ra, i + 1);
+            // bf16: a wave issuing its MFMAs goes ahead of its SIMD partner's LDS stores (measured
+            // 2-3% faster at 4096^3 and 8192 x 8192 x 4096; FP8 measured slower with it).
+            if constexpr (!kFp8) __builtin_amdgcn_s_setprio(1);
             compute(i & 1, i);
+            if constexpr (!kFp8) __builtin_amdgcn_s_setprio(0);
             if (i + 1 < steps) stage_store(ra, (i + 1) & 1);
             __syncthreads();
         }

@@ -522,10 +522,9 @@ constexpr int64_t kComputeUnits = 256;
 // one work-group per CU) when that still gives at least two rounds of work-groups; two heads when
 // the paired grid gives every compute unit a work-group; otherwise one. The host allows at most 64
 // query rows (four tiles) per KV head.
-// Heads per work-group and work-group count of the bf16 split grid.
 struct SplitShape {
-    int heads;
-    int64_t groups;
+    int heads;       // KV heads per work-group
+    int64_t groups;  // work-groups in the grid
 };
 
 SplitShape split_shape(const DecodeSplitParams& p) {

@@ -203,8 +203,8 @@ sinkattn_status sinkattn_decode_merge(const sinkattn_tensor* partial_o,
  * as one launch: every work-group writes its chunk states into `workspace`, counts itself done on
  * a per-(sequence, KV-head group) counter, and the last one to finish merges that group's chunks
  * and writes `out` (and `lse`). Larger grids, and fp32 inputs, run the split and the merge as two
- * launches on `stream` through the same workspace (the counters are not touched). The results do
- * not depend on which form runs.
+ * launches on `stream` through the same workspace (the counters are not touched). Both forms
+ * compute the same quantities; their merges may round differently in the last bits.
  *
  *   q, k, v, sinks, seqlens_k, num_chunks, scale: as for sinkattn_decode_split
  *   workspace       device memory, 256-byte aligned, at least

@@ -160,7 +160,8 @@ struct KvStage {
 };
 
 // Piece j of thread tid: index s = tid + j * 256 * kHeads over (row, head, 16-byte segment) with
-// the segment fastest, then the head (adjacent 128-byte head slices), then the row.
+// the segment fastest, then the head (adjacent 128-byte head slices), then the row. Every K/V byte
+// is read once per call, so the loads carry the non-temporal hint.
 template <int kHeads>
 __device__ __forceinline__ void stage_load(KvStage& r, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                            uint32_t k_row_bytes, uint32_t v_row_bytes, uint32_t base, int tid) {
@@ -169,8 +170,8 @@ __device__ __forceinline__ void stage_load(KvStage& r, __amdgpu_buffer_rsrc_t kr
         const int piece = tid + j * kSplitThreads * kHeads;
         const uint32_t key = base + piece / (8 * kHeads);
         const uint32_t off = 16 * (piece % (8 * kHeads));
-        r.k[j] = buffer_load_x8(krs, key * k_row_bytes + off);
-        r.v[j] = buffer_load_x8(vrs, key * v_row_bytes + off);
+        r.k[j] = buffer_load_x8_stream(krs, key * k_row_bytes + off);
+        r.v[j] = buffer_load_x8_stream(vrs, key * v_row_bytes + off);
     }
 }
 

@@ -115,6 +115,13 @@ __device__ __forceinline__ bf16x8 buffer_load_x8(__amdgpu_buffer_rsrc_t rsrc, ui
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_offset, 0, 0));
 }
 
+// The same load with the non-temporal hint (bit 1 of the cache-policy operand, `nt` on gfx950), for
+// data a kernel streams through once: the lines are not kept in the caches, which on MI355X made
+// the split-KV decode kernels' K/V stream 7-11% faster (8 x 8192 keys: 27.9 -> 25.0 us).
+__device__ __forceinline__ bf16x8 buffer_load_x8_stream(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_offset, 0, 2));
+}
+
 // acc + p[0] + p[1] in fp32 with one v_dot2c_f32_bf16 against (1, 1).
 __device__ __forceinline__ float sum_bf16x2(bf16x2 p, float acc) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};

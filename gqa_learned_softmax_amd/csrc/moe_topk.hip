@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_topk_softmax_kernel(MoeTopkPa
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             const float d = x[e] - top;
-            denom += live & (j * V + e < p.experts) ? (fast ? exp2_fast(d * kLog2e) : expf(d)) : 0.0f;
+            denom += (live & (j * V + e < p.experts)) ? (fast ? exp2_fast(d * kLog2e) : expf(d)) : 0.0f;
         }
     }
     denom = group_sum(denom);

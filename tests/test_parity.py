@@ -529,6 +529,52 @@ def test_decode_fused_bf16(name, lens, cap, chunks, hq, hkv, sr, op):
     assert torch.count_nonzero(ws[:counter_bytes]).item() == 0, "counters not reset"
 
 
+def _head_major(t):
+    """A [B, Lcap, Hkv, D] cache stored head-major ([B, Hkv, Lcap, D] memory), seen through strides."""
+    return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+
+# one-round single-head grid (8 x 8 x 4 = 256 work-groups: the single launch), a multi-round one
+# (16 x 8 x 4 = 512: split then merge), and ragged lengths with empty chunks
+@pytest.mark.parametrize("lens,chunks", [([700, 33, 1024, 0, 513, 1, 64, 999], 4),
+                                         ([700, 33, 1024, 0, 513, 1, 64, 999] * 2, 4),
+                                         ([1, 0, 333, 1024], 7)], ids=["one_round", "two_rounds", "ragged"])
+def test_decode_head_major_cache(lens, chunks):
+    sa = _sa()
+    case = workloads.make_decode(lens, 1024, chunks, seed=_seed(f"head_major_{len(lens)}_{chunks}"), poison=True)
+    q, sinks, sl = _dev(case.q, case.sinks, case.seqlens_k)
+    k, v = _head_major(case.k.cuda()), _head_major(case.v.cuda())
+    assert k.stride(2) == 1024 * 64 and not k.is_contiguous()
+    ref, rlse = oracle_decode(case)
+    po, pm, pd = sa.decode_split(q, k, v, sinks, sl, chunks, case.scale)
+    out, lse = sa.decode_merge(po, pm, pd, out_dtype=q.dtype, return_lse=True)
+    torch.cuda.synchronize()
+    check_partials(po, pm, pd, case, check_bf16, "head-major split")
+    check_bf16(out, ref, "head-major split + merge")
+    ws = sa.decode_workspace(len(lens), 64, 8, chunks, "cuda")
+    for call in range(2):
+        fout, flse = sa.decode_fused(q, k, v, sinks, sl, chunks, case.scale, ws, return_lse=True)
+        torch.cuda.synchronize()
+        check_bf16(fout, ref, f"head-major sinkattn_decode call {call}")
+        g = _np(flse)
+        assert np.array_equal(np.isneginf(g), np.isneginf(rlse))
+        fin = np.isfinite(rlse)
+        np.testing.assert_allclose(g[fin], rlse[fin], atol=1e-3)
+
+
+def test_decode_multi_head_major_cache():
+    sa = _sa()
+    case = workloads.make_decode([300, 77, 5, 1000], 1024, 4, seed=_seed("head_major_multi"), poison=True, q_len=4)
+    q, sinks, sl = _dev(case.q, case.sinks, case.seqlens_k)
+    k, v = _head_major(case.k.cuda()), _head_major(case.v.cuda())
+    po, pm, pd = sa.decode_multi_split(q, k, v, sinks, sl, 4, case.scale)
+    out = sa.decode_merge(po, pm, pd, out_dtype=q.dtype)
+    torch.cuda.synchronize()
+    check_multi_partials(po, pm, pd, case, check_bf16, "head-major multi split")
+    ref, _ = oracle_decode_multi(case)
+    check_bf16(out.view(4, 4, 64, 64), ref, "head-major multi")
+
+
 def test_decode_fused_workspace_reuse_with_smaller_problem():
     """A workspace sized for a large call serves a smaller, different call next."""
     sa = _sa()

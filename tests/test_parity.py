@@ -323,6 +323,8 @@ DECODE_SMALL = [
     ("single_kv_head", [500, 64], 512, 3, 16, 1, (-2, 2), 0.0),
     # B * Hkv/4 * C = 512 with a token-major cache: the four-KV-heads-per-work-group kernel
     ("quad_heads", [(37 * i) % 513 for i in range(32)], 512, 8, 64, 8, (-2, 2), 0.0),
+    # 1 x 8 x 20 = 160 work-groups: one round, so sinkattn_decode merges more than 16 chunks in its tail
+    ("many_chunks_one_round", [1000], 1024, 20, 64, 8, (-2, 2), 0.0),
 ]
 
 
@@ -506,7 +508,8 @@ def test_merge_many_rows_random_states(chunks, out_dtype):
 # ----------------------------------------------------------------------------- fused split + merge
 FUSED_CASES = [c for c in DECODE_SMALL if c[0] in
                ("uniform", "ragged_empty_chunks", "many_chunks", "group16", "outliers", "odd_kv_heads",
-                "single_kv_head", "paired_heads", "quad_heads", "kv_len_1", "weak_sinks")]
+                "single_kv_head", "paired_heads", "quad_heads", "kv_len_1", "weak_sinks",
+                "many_chunks_one_round")]
 
 
 @pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,sr,op", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
@@ -715,6 +718,7 @@ MULTI_CASES = [
     ("t2_quad_heads", [4 + (37 * i) % 509 for i in range(32)], 512, 8, 64, 8, 2),   # four-head work-groups
     ("t4_quad_heads", [4 + (37 * i) % 509 for i in range(32)], 512, 8, 64, 8, 4),
     ("t1_is_decode", [700, 5], 768, 4, 64, 8, 1),
+    ("t4_many_chunks_one_round", [1000], 1024, 20, 64, 8, 4),        # single launch, 20 chunks
 ]
 
 
@@ -744,7 +748,7 @@ def test_decode_multi_bf16(name, lens, cap, chunks, hq, hkv, t):
 @pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,t",
                          [c for c in MULTI_CASES if c[0] in ("t3_partial_tile", "t4_ragged_short", "t8_four_tiles",
                                                              "t4_paired_heads", "t2_quad_heads", "t4_quad_heads",
-                                                             "t6_group2")],
+                                                             "t6_group2", "t4_many_chunks_one_round")],
                          ids=lambda x: x if isinstance(x, str) else None)
 def test_decode_multi_fused_bf16(name, lens, cap, chunks, hq, hkv, t):
     sa = _sa()

@@ -116,6 +116,72 @@ def _time_graph(graph, calls, torch, replays=20):
     return per_call[mid] if replays % 2 else 0.5 * (per_call[mid - 1] + per_call[mid])
 
 
+def measure_ceilings(torch, dev):
+    """Measured ceilings (libsinkattn_ceilings, include/sinkattn_ceilings.h): the HBM streaming-read
+    rate of a plain kernel, over 2 GiB and over decode-sized 128 MiB reads rotating through that
+    buffer (more than the Infinity Cache, so every read comes from HBM); the bf16 MFMA rate of a loop
+    of independent v_mfma_f32_32x32x16_bf16 at the clock the chip holds under it; and torch's bf16
+    matmul at 8192^3 (hipBLASLt) as the practical library rate."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gqa_learned_softmax_amd", "libsinkattn_ceilings.so"))
+    lib.sinkattn_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.sinkattn_ceiling_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sinkattn_ceiling_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sinkattn_ceiling_mfma_bf16_flop.restype = ctypes.c_double
+    sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+    big = 2 * 2**30
+    buf = torch.empty(big, dtype=torch.uint8, device=dev).fill_(1)
+
+    def stream(base, nbytes, blocks):
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+        rc = lib.sinkattn_ceiling_stream_read(ctypes.c_void_p(base), nbytes, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                              ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"stream-read ceiling launch failed ({rc})")
+
+    res = {}
+    best = (0.0, 0)
+    for blocks in (1024, 2048, 4096, 8192, 16384):
+        ms = _time_graph(_capture(lambda i, b=blocks: stream(buf.data_ptr(), big, b), 3, torch), 3, torch, replays=5)
+        best = max(best, (big / (ms * 1e-3) / 1e9, blocks))
+    res["stream_read_2GiB_gbs"] = round(best[0], 1)
+    res["stream_read_2GiB_blocks"] = best[1]
+    part = 128 * 2**20
+    n_parts = big // part
+    best = (0.0, 0)
+    for blocks in (256, 512, 1024, 2048, 4096):
+        ms = _time_graph(_capture(lambda i, b=blocks: stream(buf.data_ptr() + (i % n_parts) * part, part, b), 48,
+                                  torch), 48, torch, replays=5)
+        best = max(best, (part / (ms * 1e-3) / 1e9, blocks))
+    res["stream_read_128MiB_gbs"] = round(best[0], 1)
+    res["stream_read_128MiB_blocks"] = best[1]
+    del buf
+
+    def mfma(blocks, iters):
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+        rc = lib.sinkattn_ceiling_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"MFMA ceiling launch failed ({rc})")
+
+    best = (0.0, 0)
+    for blocks in (512, 1024):  # two and four waves per SIMD
+        ms = _time_graph(_capture(lambda i, b=blocks: mfma(b, 4000), 3, torch), 3, torch, replays=5)
+        best = max(best, (lib.sinkattn_ceiling_mfma_bf16_flop(blocks, 4000) / (ms * 1e-3) / 1e12, blocks))
+    res["mfma_bf16_loop_tflops"] = round(best[0], 1)
+    res["mfma_bf16_loop_blocks"] = best[1]
+    n = 8192
+    gen = torch.Generator().manual_seed(1010)
+    a = torch.randn((n, n), generator=gen).to(torch.bfloat16).to(dev)
+    b = torch.randn((n, n), generator=gen).to(torch.bfloat16).to(dev)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    torch.matmul(a, b, out=c)
+    ms = _time_graph(_capture(lambda i: torch.matmul(a, b, out=c), 3, torch), 3, torch, replays=5)
+    res["torch_bf16_matmul_8192_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    del a, b, c
+    return res
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -127,54 +193,77 @@ def _cpu_model():
     return "unknown CPU"
 
 
-def cpu_baseline(case, kv_bytes):
-    """The oracle, as it stands, on the decode workload, over the host's cores: a pool of threads
-    (NumPy releases the interpreter lock inside its array kernels; one BLAS thread each) runs its
-    decode on one (sequence, KV head) unit at a time; whole-workload passes repeat until >= 10 s.
-    Threads, not processes, so nothing is forked from a process that has initialised the GPU.
-    Workers: the cores this process may use, at most 16."""
-    from concurrent.futures import ThreadPoolExecutor
+def _cpu_unit(task):
+    """Oracle decode of one (sequence, KV head) unit, in a worker process (see cpu_baseline)."""
+    import oracle
+    b, g = task
+    st = _CPU_STATE
+    grp = st["q"].shape[1] // st["hkv"]
+    heads = slice(g * grp, (g + 1) * grp)
+    oracle.decode(st["q"][b:b + 1, heads], st["ks"][b][:, :, g:g + 1], st["vs"][b][:, :, g:g + 1],
+                  st["sinks"][heads], [st["lens"][b]], st["scale"])
+
+
+_CPU_STATE = {}
+
+
+def cpu_baseline_worker(seconds=10.0):
+    """The oracle, as it stands, on the decode workload (regenerated from its seed), over a pool of
+    worker processes with one BLAS thread each; whole-workload passes repeat until >= ``seconds``.
+
+    Runs in a child process of its own that never touches the GPU (bench.py starts it with
+    ``--cpu-baseline-worker`` once the GPU work is done), so forking the pool is safe. Workers: the
+    cores this process may use, at most 16 (the host CPUs a one-GPU machine gives its GPU)."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    os.environ["MKL_NUM_THREADS"] = "1"
+    import multiprocessing as mp
 
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    import oracle
+    import workloads
 
-    q = case.q.double().numpy()
-    sinks = case.sinks.double().numpy()
+    case = workloads.make(2).decode
+    kv_bytes = workloads.decode_kv_bytes(case)
+    io_bytes = case.q.numel() * 2 + case.q.numel() * 2 + case.sinks.numel() * 4
     lens = [int(n) for n in case.seqlens_k.tolist()]
-    ks = [case.k[b:b + 1, :n].float().numpy() for b, n in enumerate(lens)]
-    vs = [case.v[b:b + 1, :n].float().numpy() for b, n in enumerate(lens)]
-    hkv = case.k.shape[2]
-    grp = q.shape[1] // hkv
-    tasks = [(b, g) for b in range(len(lens)) for g in range(hkv)]
+    _CPU_STATE.update(q=case.q.double().numpy(), sinks=case.sinks.double().numpy(), lens=lens,
+                      ks=[case.k[b:b + 1, :n].float().numpy() for b, n in enumerate(lens)],
+                      vs=[case.v[b:b + 1, :n].float().numpy() for b, n in enumerate(lens)],
+                      hkv=case.k.shape[2], scale=case.scale)
+    tasks = [(b, g) for b in range(len(lens)) for g in range(case.k.shape[2])]
     workers = max(1, min(len(os.sched_getaffinity(0)), 16, len(tasks)))
-
-    def unit(task):
-        b, g = task
-        heads = slice(g * grp, (g + 1) * grp)
-        oracle.decode(q[b:b + 1, heads], ks[b][:, :, g:g + 1], vs[b][:, :, g:g + 1], sinks[heads], [lens[b]],
-                      case.scale)
-
-    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as pool:
-        list(pool.map(unit, tasks))  # untimed warm-up pass
+    with threadpool_limits(limits=1), mp.get_context("fork").Pool(workers) as pool:
+        pool.map(_cpu_unit, tasks)  # untimed warm-up pass
         reps = 0
         t0 = time.perf_counter()
         while True:
-            list(pool.map(unit, tasks))
+            pool.map(_cpu_unit, tasks)
             reps += 1
             elapsed = time.perf_counter() - t0
-            if elapsed >= 10.0:
+            if elapsed >= seconds:
                 break
     return {
-        "value": round(reps * kv_bytes / elapsed / 1e9, 4),
+        "value": round(reps * (kv_bytes + io_bytes) / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"whole decode workload ({len(lens)} seqs x {max(lens)} keys, {q.shape[1]}/{hkv} heads) "
-                  f"repeated {reps}x in {elapsed:.1f} s, float64 NumPy {np.__version__}, {workers} threads x "
-                  f"1 BLAS thread, {_cpu_model()}",
+        "sample": f"whole decode workload ({len(lens)} seqs x {max(lens)} keys, {case.q.shape[1]}/{case.k.shape[2]} "
+                  f"heads) repeated {reps}x in {elapsed:.1f} s, float64 NumPy {np.__version__}, {workers} worker "
+                  f"processes x 1 BLAS thread, one (sequence, KV head) unit per task, {_cpu_model()}",
     }
+
+
+def cpu_baseline():
+    """Runs cpu_baseline_worker in a child process (started with subprocess: nothing is forked from
+    this process, which has initialised the GPU) and returns its JSON result."""
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker"],
+                         capture_output=True, text=True, timeout=600)
+    if res.returncode != 0:
+        raise RuntimeError(f"CPU baseline worker failed ({res.returncode}):\n{res.stderr[-2000:]}")
+    return json.loads(res.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -190,7 +279,12 @@ def main():
     ap.add_argument("--no-linear", action="store_true", help="skip the linear-layer detail")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the steps that reuse one K/V set (cache-resident; never the headline)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured HBM and MFMA ceilings")
+    ap.add_argument("--cpu-baseline-worker", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_worker:
+        print(json.dumps(cpu_baseline_worker()), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the hot path here is a "
               "single-GPU kernel library; no multi-GPU configuration exists.", file=sys.stderr)
@@ -221,6 +315,11 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * CALIB_BYTES / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
     del calib_src, calib_dst
+    ceilings = None
+    if not args.no_ceilings:
+        _log("measuring the HBM streaming-read and bf16 MFMA ceilings")
+        ceilings = measure_ceilings(torch, dev)
+        _log(f"ceilings: {ceilings}")
 
     # ---------------------------------------------------------------- decode workload (value)
     _log("generating decode workload (8 x 8192, 64/8 heads, bf16)")
@@ -277,6 +376,9 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    # A short spin kernel ahead of the start event keeps the GPU busy while the host submits the
+    # graph's kernels, so the events bracket the steps' GPU time and not the host's submission.
+    torch.cuda._sleep(1_000_000)
     start.record()
     steps_graph.replay()
     end.record()
@@ -339,7 +441,11 @@ def main():
             "avg_launch_us": round(ms_split * 1e3, 3),
             "measured_copy_gbs": round(copy_gbs, 1),
             "frac_of_measured_copy": round(split_gbs / copy_gbs, 4),
+            "measured_stream_read_gbs": ceilings["stream_read_128MiB_gbs"] if ceilings else None,
+            "frac_of_measured_stream_read": (round(split_gbs / ceilings["stream_read_128MiB_gbs"], 4)
+                                             if ceilings else None),
         },
+        "ceilings": ceilings,
         "decode_detail": {
             "split_us": round(ms_split * 1e3, 3), "merge_us": round(ms_merge * 1e3, 3),
             "split_plus_merge_us": round(ms_two * 1e3, 3),
@@ -350,6 +456,8 @@ def main():
             "step_us_eager_python_launch": round(ms_eager * 1e3, 3),
             "timing": "HIP graph replay of back-to-back calls, events on the replay stream",
             "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "step_frac_of_measured_stream_read": (round(value / ceilings["stream_read_128MiB_gbs"], 4)
+                                                  if ceilings else None),
         },
     }
 
@@ -405,7 +513,7 @@ def main():
         for i in range(max(2, args.warmup // 2)):
             prefill(i)
         n_pre = max(5, args.steps // 2)
-        ms_pre = _time_graph(_capture(prefill, n_pre, torch), n_pre, torch, replays=2)
+        ms_pre = _time_graph(_capture(prefill, n_pre, torch), n_pre, torch, replays=7)
         tflops = flops / (ms_pre * 1e-3) / 1e12
         _log(f"prefill {ms_pre * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
         result["prefill"] = {
@@ -416,7 +524,10 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "prefill_bf16", "achieved": round(tflops, 2),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                         "algorithmic_flop_per_launch": flops},
+                         "algorithmic_flop_per_launch": flops,
+                         "measured_mfma_loop_tflops": ceilings["mfma_bf16_loop_tflops"] if ceilings else None,
+                         "frac_of_measured_mfma_loop": (round(tflops / ceilings["mfma_bf16_loop_tflops"], 4)
+                                                        if ceilings else None)},
         }
 
     # ---------------------------------------------------------------- split-KV (append) prefill
@@ -443,8 +554,8 @@ def main():
             sa.decode_merge(apo, apm, apd, out=aout)
 
         n_app = max(5, args.steps // 2)
-        ms_plain = _time_graph(_capture(app_plain, n_app, torch), n_app, torch, replays=2)
-        ms_split = _time_graph(_capture(app_split, n_app, torch), n_app, torch, replays=2)
+        ms_plain = _time_graph(_capture(app_plain, n_app, torch), n_app, torch, replays=5)
+        ms_split = _time_graph(_capture(app_split, n_app, torch), n_app, torch, replays=5)
         _log(f"append prefill: unsplit {ms_plain * 1e3:.1f} us, {splits}-way KV split + merge "
              f"{ms_split * 1e3:.1f} us")
         result["prefill_append"] = {
@@ -598,7 +709,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
         _log("timing the CPU oracle on the decode workload over the host cores (~10 s)")
-        result["cpu_baseline"] = cpu_baseline(case, step_bytes)
+        result["cpu_baseline"] = cpu_baseline()
     else:
         result["cpu_baseline"] = None
 

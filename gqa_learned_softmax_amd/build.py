@@ -1,7 +1,8 @@
 """Builds libsinkattn.so (the C-ABI HIP library) in-tree with hipcc for gfx950.
 
 Usage: ``python gqa_learned_softmax_amd/build.py`` (or ``__graft_entry__.build()``). Sources are
-compiled to objects in parallel, then linked into ``gqa_learned_softmax_amd/libsinkattn.so``.
+compiled to objects in parallel, then linked into ``gqa_learned_softmax_amd/libsinkattn.so``; the
+measurement kernels (``csrc/ceilings.hip``) go into ``libsinkattn_ceilings.so`` beside it.
 Every call recompiles.
 """
 from __future__ import annotations
@@ -20,6 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libsinkattn.so")
 
 SOURCES = ["api.cpp", "decode_split.hip", "decode_merge.hip", "prefill.hip", "moe_topk.hip", "gemm.hip"]
+CEILING_SOURCES = ["ceilings.hip"]
+CEILINGS_LIB_PATH = os.path.join(PKG_DIR, "libsinkattn_ceilings.so")
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -47,19 +50,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every source and link libsinkattn.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as pool:
-        objs = list(pool.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Compile every source and link libsinkattn.so and libsinkattn_ceilings.so; returns the
+    path of libsinkattn.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    sources = SOURCES + CEILING_SOURCES
+    with ThreadPoolExecutor(max_workers=min(4, len(sources))) as pool:
+        objs = list(pool.map(lambda s: _compile(s, list(extra_flags)), sources))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], CEILINGS_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {CEILINGS_LIB_PATH}")
     return LIB_PATH
 
 

@@ -98,17 +98,17 @@ __device__ __forceinline__ void tile_softmax(const f32x4 (&s)[4], float& m, floa
         }
 }
 
-// Completion of the fused kernels: every work-group has written its chunk states (write-through
-// stores); it counts itself done on the counter of its (sequence, KV-head set), and the last one to
-// arrive merges all chunks of the set's query rows (set_rows heads x T tokens) and writes out/lse.
-// The barrier orders every wave's stores before thread 0's device-scope release fence (an L2
-// write-back); only the last arrival takes the acquire fence (an L2 and L1 invalidate), after which
-// it reads every chunk's states whichever XCD produced them. Each wave merges four rows at a time
-// (measured 0.7 us faster than one row per wave on 8 x 8192 keys, one token).
+// Completion of the fused kernels. Wave 0 has written every chunk state of the work-group with
+// write-through stores; thread 0 (in that wave) takes a device-scope release fence (on gfx950 an L2
+// write-back plus a wait for the wave's outstanding stores, so all of them are complete) and counts
+// the work-group done on the counter of its (sequence, KV-head set). The last one to arrive merges
+// all chunks of the set's query rows (set_rows heads x T tokens) and writes out/lse. Only the last
+// arrival takes the acquire fence (an L2 and L1 invalidate), after which it reads every chunk's
+// states whichever XCD produced them. Each wave merges four rows at a time (measured 0.7 us faster
+// than one row per wave on 8 x 8192 keys, one token).
 template <int kWaves>
 __device__ __forceinline__ void fused_merge_tail(const DecodeSplitParams& p, int b, int head_set, int set_rows,
                                                  int heads_per_row, int wave_all, int& last_arrival) {
-    __syncthreads();
     uint32_t* counter = p.counters + static_cast<int64_t>(b) * heads_per_row + head_set;
     if (threadIdx.x == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -414,29 +414,59 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     const float m_nat = d_tot > 0.0f ? m * kLn2 : kNegInf;
     const int64_t row = ((static_cast<int64_t>(b) * q_len + tok) * p.num_q_heads + head) * p.num_chunks + chunk;
     if constexpr (kFused) {
-        // Write-through stores (the release fence in the tail then has no dirty L2 lines to write
-        // back). The O^T tile goes through LDS first, so that every store instruction writes one
-        // contiguous 256-byte row of partial_o; the K tiles are free after the loop's last barrier.
-        static_assert(sizeof(k_lds) >= sizeof(float) * kWaves * 16 * (kHeadDim + 4), "staging space");
-        float (*ot)[kHeadDim + 4] = reinterpret_cast<float (*)[kHeadDim + 4]>(&k_lds[0][0][0][0]) + 16 * wave_all;
+        // Every chunk state of the work-group goes through LDS (the K tiles are free after the
+        // loop's last barrier) and wave 0 alone writes them all with write-through stores, one
+        // contiguous 256-byte row of partial_o per store instruction; the release fence of that
+        // same wave in fused_merge_tail then orders all of them before the arrival count.
+        constexpr int kOPitch = kHeadDim + 4;
+        static_assert(sizeof(k_lds) >= sizeof(float) * kWaves * 16 * (kOPitch + 2), "staging space");
+        float (*ot_all)[kOPitch] = reinterpret_cast<float (*)[kOPitch]>(&k_lds[0][0][0][0]);
+        float* md_all = reinterpret_cast<float*>(&k_lds[0][0][0][0]) + kWaves * 16 * kOPitch;
         if (writes_state) {
+            float (*ot)[kOPitch] = ot_all + 16 * wave_all;
 #pragma unroll
             for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(&ot[col][16 * n + 4 * grp]) = acc[n] * inv;
-            if (col_valid && grp == 0) {
-                __hip_atomic_store(&p.partial_m[row], m_nat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                __hip_atomic_store(&p.partial_d[row], d_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (grp == 0) {
+                md_all[(2 * wave_all) * 16 + col] = m_nat;
+                md_all[(2 * wave_all + 1) * 16 + col] = d_tot;
             }
         }
         __syncthreads();
-        if (writes_state) {
-            const int tile_cols = columns - 16 * tile < 16 ? columns - 16 * tile : 16;
-            for (int r = 0; r < tile_cols; ++r) {
-                const int cr = 16 * tile + r;
-                const int64_t row_r =
-                    ((static_cast<int64_t>(b) * q_len + cr / group) * p.num_q_heads + g * group + cr % group) *
-                        p.num_chunks + chunk;
-                __hip_atomic_store(&p.partial_o[row_r * kHeadDim + lane], ot[r][lane], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        if (wave_all == 0) {
+            for (int w = 0; w < kWaves; ++w) {
+                const int w_tile = w % kSplitWaves;
+                const bool w_writes = kKeySplit ? w_tile == 0 : 16 * w_tile < columns;
+                if (!w_writes) continue;
+                const int w_g = head_set * kHeads + w / kSplitWaves;
+                const int c0 = kKeySplit ? 0 : 16 * w_tile;
+                const int tile_cols = columns - c0 < 16 ? columns - c0 : 16;
+                auto state_row = [&](int r) {
+                    const int cr = c0 + r;
+                    return ((static_cast<int64_t>(b) * q_len + cr / group) * p.num_q_heads + w_g * group + cr % group) *
+                               p.num_chunks + chunk;
+                };
+                // Two rows per store instruction (8 bytes a lane); all LDS reads of the tile are
+                // issued before its stores, so the wave waits for LDS once per tile.
+                uint64_t two[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 2 * i + (lane >> 5);
+                    two[i] = r < tile_cols ? *reinterpret_cast<const uint64_t*>(&ot_all[16 * w + r][2 * (lane & 31)]) : 0;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 2 * i + (lane >> 5);
+                    if (r < tile_cols)
+                        __hip_atomic_store(reinterpret_cast<uint64_t*>(&p.partial_o[state_row(r) * kHeadDim + 2 * (lane & 31)]),
+                                           two[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+                if (lane < tile_cols) {
+                    const int64_t row_l = state_row(lane);
+                    __hip_atomic_store(&p.partial_m[row_l], md_all[(2 * w) * 16 + lane], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_SYSTEM);
+                    __hip_atomic_store(&p.partial_d[row_l], md_all[(2 * w + 1) * 16 + lane], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_SYSTEM);
+                }
             }
         }
     } else if (writes_state && col_valid) {

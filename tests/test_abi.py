@@ -59,6 +59,36 @@ def test_every_declared_function_is_exported():
     assert names == set(_lib.EXPORTS)
 
 
+CEILINGS_HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sinkattn_ceilings.h")
+CEILINGS_LIB = os.path.join(os.path.dirname(_lib.LIB_PATH), "libsinkattn_ceilings.so")
+
+
+def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
+    """The measurement library loads, exports what include/sinkattn_ceilings.h declares, and
+    rejects invalid arguments on the host (return 1) without launching anything."""
+    text = open(CEILINGS_HEADER).read()
+    names = set(re.findall(r"^\s*(?:int|double)\s+(sinkattn_ceiling_\w+)\s*\(", text, flags=re.M))
+    assert names == {"sinkattn_ceiling_stream_read", "sinkattn_ceiling_mfma_bf16",
+                     "sinkattn_ceiling_mfma_bf16_flop"}
+    lib = ctypes.CDLL(CEILINGS_LIB)
+    for name in names:
+        assert hasattr(lib, name), name
+    lib.sinkattn_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.sinkattn_ceiling_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sinkattn_ceiling_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sinkattn_ceiling_mfma_bf16_flop.restype = ctypes.c_double
+    fake = 1 << 40
+    assert lib.sinkattn_ceiling_stream_read(None, 1 << 20, 64, fake, None) == 1
+    assert lib.sinkattn_ceiling_stream_read(fake, (1 << 20) + 8, 64, fake, None) == 1  # not whole 16 B
+    assert lib.sinkattn_ceiling_stream_read(fake + 8, 1 << 20, 64, fake, None) == 1    # misaligned
+    assert lib.sinkattn_ceiling_stream_read(fake, 1 << 20, 0, fake, None) == 1
+    assert lib.sinkattn_ceiling_mfma_bf16(0, 10, fake, None) == 1
+    assert lib.sinkattn_ceiling_mfma_bf16(8, 0, fake, None) == 1
+    # 4 waves x 4 MFMAs of 32 x 32 x 16 x 2 flop per block and iteration.
+    assert lib.sinkattn_ceiling_mfma_bf16_flop(3, 5) == 3 * 5 * 4 * 4 * 32 * 32 * 16 * 2
+
+
 def test_version_and_status_strings():
     text = open(HEADER).read()
     version = int(re.search(r"#define SINKATTN_VERSION (\d+)", text).group(1))

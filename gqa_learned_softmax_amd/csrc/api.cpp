@@ -333,10 +333,10 @@ sinkattn_status check_prefill_inputs(const sinkattn_tensor* q, const sinkattn_te
                     (long long)group);
     if (tq >= (int64_t(1) << 31) || tk >= (int64_t(1) << 31) || num_seqs >= (int64_t(1) << 24))
         return fail(SINKATTN_ERR_UNSUPPORTED, "token or sequence count too large");
-    // Key rows are addressed with 32-bit byte offsets, including prefetches up to 128 rows past
-    // a sequence's end.
-    if ((tk + 128) * k->stride[0] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
-        (tk + 128) * v->stride[0] * elem_size(v->dtype) >= (int64_t(1) << 31))
+    // Key rows are addressed with 32-bit byte offsets, including prefetches up to 192 rows past
+    // a sequence's end (two 64-key tiles ahead of the last one).
+    if ((tk + 192) * k->stride[0] * elem_size(k->dtype) >= (int64_t(1) << 31) ||
+        (tk + 192) * v->stride[0] * elem_size(v->dtype) >= (int64_t(1) << 31))
         return fail(SINKATTN_ERR_UNSUPPORTED, "K/V exceed 2 GiB of addressable rows");
     SA_TRY(check_data(q, "q"));
     SA_TRY(check_data(k, "k"));

@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import SinkAttnError  # noqa: F401
 
 __all__ = ["prefill", "prefill_split", "prefill_kv_split", "decode_split", "decode_merge", "decode",
-           "decode_fused", "decode_workspace", "decode_multi_split", "decode_multi", "decode_multi_fused",
+           "decode_fused", "decode_workspace", "decode_static", "decode_multi_split", "decode_multi", "decode_multi_fused",
            "moe_topk_softmax", "linear_bias", "linear_fp8_block_scaled", "SinkAttnError", "version"]
 
 
@@ -124,6 +124,22 @@ def decode_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, out=No
         _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
         int(num_chunks), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_static(q, k, v, sinks, seqlens_k, num_chunks, scale, out=None, lse=None, return_lse=False):
+    """``sinkattn_decode_static``: as ``decode_fused`` with the library's own device workspace
+    (nothing allocated by the library; ``out``/``lse`` are allocated here when not given)."""
+    batch, hq, dim = q.shape
+    if out is None:
+        out = torch.empty((batch, hq, dim), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    dev = _lib.require_device(q, k, v, sinks, seqlens_k, out, lse)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k, out, lse)]
+    _lib.check(_lib.lib.sinkattn_decode_static(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        int(num_chunks), float(scale), _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

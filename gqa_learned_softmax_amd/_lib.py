@@ -68,6 +68,8 @@ EXPORTS = {
                          ctypes.c_size_t, _P, _P, ctypes.c_void_p], ctypes.c_int),
     "sinkattn_decode_multi": ([_P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                ctypes.c_size_t, _P, _P, ctypes.c_void_p], ctypes.c_int),
+    "sinkattn_decode_static": ([_P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, ctypes.c_void_p],
+                               ctypes.c_int),
     "sinkattn_decode_workspace_size": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int],
                                        ctypes.c_size_t),
     "sinkattn_decode_workspace_counter_bytes": ([ctypes.c_int64, ctypes.c_int64], ctypes.c_size_t),

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libsinkattn.so")
 
-SOURCES = ["api.cpp", "decode_split.hip", "decode_merge.hip", "prefill.hip", "moe_topk.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "decode_split.hip", "decode_merge.hip", "prefill.hip", "moe_topk.hip", "gemm.hip",
+           "static_workspace.hip"]
 CEILING_SOURCES = ["ceilings.hip"]
 CEILINGS_LIB_PATH = os.path.join(PKG_DIR, "libsinkattn_ceilings.so")
 

@@ -422,12 +422,14 @@ sinkattn_status decode_split_impl(const sinkattn_tensor* q, const sinkattn_tenso
 
 // sinkattn_decode (q, out [B, Hq, D], lse [B, Hq]) and sinkattn_decode_multi (q, out [B, T, Hq, D],
 // lse [B, T, Hq]); the workspace holds the partials of B x T rows.
+// With static_ws, the workspace is the library's own device array (sinkattn_decode_static):
+// workspace/workspace_bytes are ignored and the call allocates nothing.
 sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tensor* k,
                                   const sinkattn_tensor* v, const sinkattn_tensor* sinks,
                                   const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
                                   void* workspace, size_t workspace_bytes,
                                   const sinkattn_tensor* out, const sinkattn_tensor* lse,
-                                  void* stream, bool multi) {
+                                  void* stream, bool multi, bool static_ws = false) {
     g_last_error.clear();
     const int rank = multi ? 4 : 3;
     SA_TRY(check_desc(q, "q", rank));
@@ -447,11 +449,19 @@ sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tenso
             return fail(SINKATTN_ERR_SHAPE, multi ? "lse: expected [B, T, Hq]" : "lse: expected [B, Hq]");
     const WorkspaceLayout w =
         workspace_layout(static_cast<int64_t>(p.batch) * p.q_len, p.num_q_heads, p.num_kv_heads, num_chunks);
-    if (workspace_bytes < w.total)
-        return fail(SINKATTN_ERR_SHAPE, "workspace: %zu bytes, need %zu", workspace_bytes, w.total);
-    if (w.total > 0 && workspace == nullptr) return fail(SINKATTN_ERR_NULL, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-        return fail(SINKATTN_ERR_LAYOUT, "workspace not 256-byte aligned");
+    if (static_ws) {
+        if (w.total > sinkattn::kStaticWorkspaceBytes)
+            return fail(SINKATTN_ERR_UNSUPPORTED,
+                        "chunk states need %zu bytes, more than the %zu-byte static workspace "
+                        "(use sinkattn_decode with a workspace of that size)",
+                        w.total, sinkattn::kStaticWorkspaceBytes);
+    } else {
+        if (workspace_bytes < w.total)
+            return fail(SINKATTN_ERR_SHAPE, "workspace: %zu bytes, need %zu", workspace_bytes, w.total);
+        if (w.total > 0 && workspace == nullptr) return fail(SINKATTN_ERR_NULL, "workspace is NULL");
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            return fail(SINKATTN_ERR_LAYOUT, "workspace not 256-byte aligned");
+    }
     SA_TRY(check_data(out, "out"));
     SA_TRY(check_rows(out, "out"));
     SA_TRY(check_no_self_overlap(out, "out"));
@@ -463,7 +473,8 @@ sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tenso
             return fail(SINKATTN_ERR_LAYOUT, "lse: innermost stride must be 1");
         SA_TRY(check_no_self_overlap(lse, "lse"));
     }
-    // The workspace is written too: it may not overlap any tensor argument.
+    // The workspace is written too: it may not overlap any tensor argument (the static one is
+    // the library's own memory, which no argument can point into).
     sinkattn_tensor ws{};
     ws.data = workspace;
     ws.dtype = SINKATTN_F32;
@@ -474,16 +485,18 @@ sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tenso
     const char* inames[5] = {"q", "k", "v", "sinks", "seqlens_k"};
     for (int b = 0; b < 5; ++b) {
         SA_TRY(check_disjoint(out, "out", ins[b], inames[b]));
-        SA_TRY(check_disjoint(&ws, "workspace", ins[b], inames[b]));
+        if (!static_ws) SA_TRY(check_disjoint(&ws, "workspace", ins[b], inames[b]));
         if (lse != nullptr) SA_TRY(check_disjoint(lse, "lse", ins[b], inames[b]));
     }
-    SA_TRY(check_disjoint(out, "out", &ws, "workspace"));
+    if (!static_ws) SA_TRY(check_disjoint(out, "out", &ws, "workspace"));
     if (lse != nullptr) {
-        SA_TRY(check_disjoint(lse, "lse", &ws, "workspace"));
+        if (!static_ws) SA_TRY(check_disjoint(lse, "lse", &ws, "workspace"));
         SA_TRY(check_disjoint(out, "out", lse, "lse"));
     }
 
     if (p.batch == 0 || p.q_len == 0) return SINKATTN_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (static_ws) SA_TRY(launched(sinkattn::static_decode_workspace(s, &workspace)));
     char* base = static_cast<char*>(workspace);
     p.counters = reinterpret_cast<uint32_t*>(base + w.counters);
     p.partial_o = reinterpret_cast<float*>(base + w.partial_o);
@@ -498,7 +511,6 @@ sinkattn_status decode_fused_impl(const sinkattn_tensor* q, const sinkattn_tenso
     p.lse_stride_tok = lse != nullptr && multi ? lse->stride[1] : 0;
     p.lse_stride_head = lse != nullptr ? lse->stride[rank - 2] : 0;
     p.out_is_bf16 = out->dtype == SINKATTN_BF16;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = q->dtype == SINKATTN_BF16;
     // One launch when the split grid fits a single round of work-groups; otherwise (and for the
     // fp32 reference variant) split then merge through the same workspace, which leaves the
@@ -749,6 +761,17 @@ sinkattn_status sinkattn_decode_multi(const sinkattn_tensor* q, const sinkattn_t
                                       void* stream) {
     return decode_fused_impl(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace,
                              workspace_bytes, out, lse, stream, true);
+}
+
+sinkattn_status sinkattn_decode_static(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                       const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                       const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                       const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                       void* stream) {
+    static_assert(SINKATTN_DECODE_STATIC_WORKSPACE_BYTES == sinkattn::kStaticWorkspaceBytes,
+                  "header and library agree on the static workspace size");
+    return decode_fused_impl(q, k, v, sinks, seqlens_k, num_chunks, scale, nullptr, 0, out, lse, stream,
+                             /*multi=*/false, /*static_ws=*/true);
 }
 
 size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,

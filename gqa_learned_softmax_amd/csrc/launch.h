@@ -100,4 +100,10 @@ hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stre
 bool decode_fused_fits_one_round(const DecodeSplitParams& p);
 hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream);
 
+// sinkattn_decode_static: the library-owned workspace, one per GPU (static_workspace.hip).
+constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
+// Device address of the current device's copy; the first call on a device looks it up and clears
+// it with a kernel on `stream`.
+hipError_t static_decode_workspace(hipStream_t stream, void** out);
+
 }  // namespace sinkattn

@@ -272,6 +272,31 @@ sinkattn_status sinkattn_decode_multi(const sinkattn_tensor* q, const sinkattn_t
                                       void* workspace, size_t workspace_bytes,
                                       const sinkattn_tensor* out, const sinkattn_tensor* lse,
                                       void* stream);
+/*
+ * sinkattn_decode_static - sinkattn_decode without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. The call allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * The chunk states and arrival counters live in a device array owned by the library,
+ * SINKATTN_DECODE_STATIC_WORKSPACE_BYTES bytes on each GPU it runs on, held from the time the
+ * library's code is loaded until the process ends. The first call on a device (the current one)
+ * looks its address up and clears it with one kernel on `stream`, ahead of the call's own kernels;
+ * every completed call leaves its counters zero again. All calls on one GPU share that array, so
+ * calls that overlap in time on one GPU (other streams, other host threads) race and give wrong
+ * results; serialise them.
+ *
+ * Arguments, results and limits as for sinkattn_decode (one token per sequence), plus: a problem
+ * whose chunk states need more than SINKATTN_DECODE_STATIC_WORKSPACE_BYTES
+ * (sinkattn_decode_workspace_size(B, Hq, Hkv, num_chunks) bytes) returns SINKATTN_ERR_UNSUPPORTED
+ * before anything is launched. B = 0 launches nothing and does not touch the device.
+ */
+#define SINKATTN_DECODE_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+sinkattn_status sinkattn_decode_static(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                       const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                       const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                       const sinkattn_tensor* out, const sinkattn_tensor* lse,
+                                       void* stream);
+
 /* Bytes of workspace sinkattn_decode needs (0 for invalid arguments). */
 size_t sinkattn_decode_workspace_size(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
                                       int num_chunks);

@@ -371,6 +371,52 @@ def test_fused_rejects(name, mutate, code):
     assert last_error()
 
 
+# ----------------------------------------------------------------------------- decode, static workspace
+def call_static(a):
+    return _lib.lib.sinkattn_decode_static(R(a["q"]), R(a["k"]), R(a["v"]), R(a["sinks"]), R(a["seqlens"]),
+                                           a["chunks"], a["scale"], R(a["out"]), R(a["lse"]), None)
+
+
+def test_static_decode_header_limit_matches_the_workspace_formula():
+    text = open(HEADER).read()
+    limit = re.search(r"#define SINKATTN_DECODE_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert limit, "SINKATTN_DECODE_STATIC_WORKSPACE_BYTES"
+    assert int(limit.group(1)) << int(limit.group(2)) == 32 << 20
+    # The 8 x 8192-key decode (64/8 heads, 8 chunks) and the 128-sequence mixed decode fit; a
+    # problem one chunk-state row larger than the limit does not.
+    assert _lib.lib.sinkattn_decode_workspace_size(8, 64, 8, 8) <= 32 << 20
+    assert _lib.lib.sinkattn_decode_workspace_size(128, 64, 8, 8) <= 32 << 20
+
+
+def test_static_decode_empty_batch_touches_nothing():
+    # B = 0 returns before any HIP call (this container has no GPU).
+    assert call_static(fused_args(b=0)) == _lib.OK
+
+
+def test_static_decode_rejects_problems_beyond_its_workspace():
+    # 128 sequences x 64 heads x 64 chunks of 66 floats: 138 MB of chunk states.
+    a = fused_args(b=128, hq=64, hkv=8, cap=4096, chunks=64)
+    assert call_static(a) == _lib.ERR_UNSUPPORTED, last_error()
+    assert "static workspace" in last_error()
+
+
+STATIC_CASES = [
+    ("out_shape", lambda a: _mut(a, out=T([2, 4, 64])), _lib.ERR_SHAPE),
+    ("out_int", lambda a: _mut(a, out=T([2, 8, 64], I32)), _lib.ERR_DTYPE),
+    ("lse_overlaps_out", lambda a: _mut(a, lse=T([2, 8], F32, addr=a["out"].data)), _lib.ERR_LAYOUT),
+    ("out_overlaps_k", lambda a: _mut(a, out=T([2, 8, 64], addr=a["k"].data)), _lib.ERR_LAYOUT),
+    ("chunks_zero", lambda a: _mut(a, chunks=0), _lib.ERR_SHAPE),
+    ("group_32", lambda a: fused_args(hq=32), _lib.ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", STATIC_CASES, ids=[c[0] for c in STATIC_CASES])
+def test_static_decode_rejects(name, mutate, code):
+    status = call_static(mutate(fused_args()))
+    assert status == code, (status, last_error())
+    assert last_error()
+
+
 # ----------------------------------------------------------------------------- multi-token decode
 def msplit_args(b=2, t=3, hq=8, hkv=1, cap=64, chunks=4, dim=64, dtype=BF16):
     return dict(q=T([b, t, hq, dim], dtype), k=T([b, cap, hkv, dim], dtype), v=T([b, cap, hkv, dim], dtype),

@@ -410,6 +410,8 @@ def main():
          + (f", hot step {ms_hot * 1e3:.2f} us" if ms_hot else ""))
 
     traffic = _traffic_from_profile(_source_hash(SPLIT_SOURCES))
+    # The kernel the split call dispatches for this shape, as the library reports it.
+    (split_launch,) = sa.plan_decode(q, k0, v0, sinks, seqlens, chunks, case.scale, form="split")
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -431,7 +433,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_bf16_kernel<2, false, true>",
+            "kernel": split_launch["kernel"],
+            "grid": split_launch["grid"],
             "achieved": round(split_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -521,7 +524,9 @@ def main():
             "ms_per_call": round(ms_pre, 4),
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
-            "roofline": {"bound": "mfma", "kernel": "prefill_bf16", "achieved": round(tflops, 2),
+            "roofline": {"bound": "mfma",
+                         "kernel": sa.plan_prefill(pq, pk, pv, ps, pcq, pck, pre.scale, True)[0]["kernel"],
+                         "achieved": round(tflops, 2),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                          "algorithmic_flop_per_launch": flops,

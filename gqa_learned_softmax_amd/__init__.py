@@ -9,6 +9,8 @@ stream. Allocation of outputs (when not given) is the only other thing done here
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -16,7 +18,8 @@ from ._lib import SinkAttnError  # noqa: F401
 
 __all__ = ["prefill", "prefill_split", "prefill_kv_split", "decode_split", "decode_merge", "decode",
            "decode_fused", "decode_workspace", "decode_static", "decode_multi_split", "decode_multi", "decode_multi_fused",
-           "moe_topk_softmax", "linear_bias", "linear_fp8_block_scaled", "SinkAttnError", "version"]
+           "moe_topk_softmax", "linear_bias", "linear_fp8_block_scaled", "plan_decode", "plan_prefill",
+           "SinkAttnError", "version"]
 
 
 def version() -> int:
@@ -191,6 +194,38 @@ def decode_multi_fused(q, k, v, sinks, seqlens_k, num_chunks, scale, workspace, 
         int(num_chunks), float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _lib.ref(d[5]), _lib.ref(d[6]), _lib.stream_handle(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def _launches(buf, count):
+    return [{"kernel": buf[i].kernel.decode(), "grid": int(buf[i].grid), "block": int(buf[i].block)}
+            for i in range(count.value)]
+
+
+def plan_decode(q, k, v, sinks, seqlens_k, num_chunks, scale, form="split"):
+    """``sinkattn_plan_decode``: the launches of ``decode_split`` / ``decode_multi_split``
+    (``form="split"``) or of ``decode_fused`` / ``decode_multi_fused`` / ``decode_static``
+    (``form="decode"``) for these inputs, as ``[{"kernel", "grid", "block"}, ...]``. Nothing is
+    launched and no tensor is read, so CPU tensors of the right shapes and strides will do."""
+    forms = {"split": _lib.PLAN_DECODE_SPLIT, "decode": _lib.PLAN_DECODE}
+    buf = (_lib.Launch * 2)()
+    count = ctypes.c_int(0)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, seqlens_k)]
+    _lib.check(_lib.lib.sinkattn_plan_decode(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]),
+        int(num_chunks), float(scale), forms[form], buf, ctypes.byref(count)))
+    return _launches(buf, count)
+
+
+def plan_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal=True, num_splits=0):
+    """``sinkattn_plan_prefill``: the launch of ``prefill`` (``num_splits=0``) or of
+    ``prefill_split`` for these inputs (CPU tensors will do, as for ``plan_decode``)."""
+    buf = (_lib.Launch * 1)()
+    count = ctypes.c_int(0)
+    d = [_lib.describe(t) for t in (q, k, v, sinks, cu_seqlens_q, cu_seqlens_k)]
+    _lib.check(_lib.lib.sinkattn_plan_prefill(
+        _lib.ref(d[0]), _lib.ref(d[1]), _lib.ref(d[2]), _lib.ref(d[3]), _lib.ref(d[4]), _lib.ref(d[5]),
+        float(scale), 1 if causal else 0, int(num_splits), buf, ctypes.byref(count)))
+    return _launches(buf, count)
 
 
 def moe_topk_softmax(logits, top_k, over_all_experts=False, ids=None, weights=None,

@@ -11,7 +11,10 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsinkattn.so")
+# The library this module binds. SINKATTN_LIBRARY names another build of the same C ABI instead
+# (a debug build of the kernels, or the host-only build used to check the ABI layer without a GPU).
+DEFAULT_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsinkattn.so")
+LIB_PATH = os.environ.get("SINKATTN_LIBRARY") or DEFAULT_LIB_PATH
 
 # sinkattn_status
 OK = 0
@@ -54,6 +57,20 @@ class Tensor(ctypes.Structure):
 
 _P = ctypes.POINTER(Tensor)
 
+
+class Launch(ctypes.Structure):
+    """``sinkattn_launch``."""
+
+    _fields_ = [("kernel", ctypes.c_char * 96), ("grid", ctypes.c_int64), ("block", ctypes.c_int32)]
+
+
+_L = ctypes.POINTER(Launch)
+_IP = ctypes.POINTER(ctypes.c_int)
+
+# sinkattn_plan_form
+PLAN_DECODE_SPLIT = 0
+PLAN_DECODE = 1
+
 EXPORTS = {
     "sinkattn_prefill": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int, _P, ctypes.c_void_p],
                          ctypes.c_int),
@@ -77,17 +94,22 @@ EXPORTS = {
     "sinkattn_linear_bias": ([_P, _P, _P, _P, ctypes.c_void_p], ctypes.c_int),
     "sinkattn_linear_fp8_block_scaled": ([_P, _P, _P, _P, _P, _P, ctypes.c_void_p], ctypes.c_int),
     "sinkattn_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "sinkattn_plan_decode": ([_P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_int, _L, _IP],
+                             ctypes.c_int),
+    "sinkattn_plan_prefill": ([_P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int, ctypes.c_int, _L, _IP],
+                              ctypes.c_int),
     "sinkattn_last_error": ([], ctypes.c_char_p),
     "sinkattn_version": ([], ctypes.c_int),
 }
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def load(path: str) -> ctypes.CDLL:
+    """Loads a build of the C ABI at ``path`` and declares every exported function's types."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python gqa_learned_softmax_amd/build.py` "
+            f"{path} is not built; run `python gqa_learned_softmax_amd/build.py` "
             "(or __graft_entry__.build()) first")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     for name, (argtypes, restype) in EXPORTS.items():
         fn = getattr(lib, name)
         fn.argtypes = argtypes
@@ -95,7 +117,7 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-lib = _load()
+lib = load(LIB_PATH)
 
 
 def describe(t: torch.Tensor | None) -> Tensor | None:

@@ -8,10 +8,12 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "launch.h"
 #include "launch_ops.h"
+#include "plan.h"
 
 namespace {
 
@@ -33,7 +35,7 @@ sinkattn_status fail(sinkattn_status status, const char* fmt, ...) {
         if (_s != SINKATTN_OK) return _s;         \
     } while (0)
 
-int64_t elem_size(sinkattn_dtype dt) {
+int64_t elem_size(int32_t dt) {
     switch (dt) {
         case SINKATTN_F32: return 4;
         case SINKATTN_BF16: return 2;
@@ -43,7 +45,7 @@ int64_t elem_size(sinkattn_dtype dt) {
     return 0;
 }
 
-const char* dtype_name(sinkattn_dtype dt) {
+const char* dtype_name(int32_t dt) {
     switch (dt) {
         case SINKATTN_F32: return "f32";
         case SINKATTN_BF16: return "bf16";
@@ -80,7 +82,7 @@ sinkattn_status check_data(const sinkattn_tensor* t, const char* name) {
     return SINKATTN_OK;
 }
 
-sinkattn_status check_dtype(const sinkattn_tensor* t, const char* name, sinkattn_dtype want) {
+sinkattn_status check_dtype(const sinkattn_tensor* t, const char* name, int32_t want) {
     if (t->dtype != want)
         return fail(SINKATTN_ERR_DTYPE, "%s: dtype %s, expected %s", name, dtype_name(t->dtype),
                     dtype_name(want));
@@ -190,6 +192,13 @@ sinkattn_status launched(hipError_t err) {
     if (err != hipSuccess)
         return fail(SINKATTN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(err));
     return SINKATTN_OK;
+}
+
+void put_launch(sinkattn_launch& dst, const sinkattn::Launch& src) {
+    static_assert(sizeof(dst.kernel) == sizeof(src.kernel), "kernel name buffers");
+    memcpy(dst.kernel, src.kernel, sizeof(dst.kernel));
+    dst.grid = src.grid;
+    dst.block = src.block;
 }
 
 // Largest G x T query rows per KV head the multi-token decode kernel takes (four 16-column tiles).
@@ -957,6 +966,69 @@ const char* sinkattn_status_string(sinkattn_status status) {
 }
 
 const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
+
+sinkattn_status sinkattn_plan_decode(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                     const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                     const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                     int form, sinkattn_launch* launches, int* count) {
+    g_last_error.clear();
+    if (launches == nullptr || count == nullptr) return fail(SINKATTN_ERR_NULL, "launches/count is NULL");
+    *count = 0;
+    if (form != SINKATTN_PLAN_DECODE_SPLIT && form != SINKATTN_PLAN_DECODE)
+        return fail(SINKATTN_ERR_SHAPE, "unknown plan form %d", form);
+    if (q == nullptr) return fail(SINKATTN_ERR_NULL, "q is NULL");
+    const bool multi = q->ndim == 4;
+    sinkattn::DecodeSplitParams p{};
+    SA_TRY(check_decode_inputs(q, k, v, sinks, seqlens_k, num_chunks, scale, multi, p));
+    if (p.batch == 0 || p.q_len == 0) return SINKATTN_OK;
+    const bool bf16 = q->dtype == SINKATTN_BF16;
+    if (form == SINKATTN_PLAN_DECODE && bf16 && sinkattn::decode_fused_fits_one_round(p)) {
+        put_launch(launches[0], sinkattn::plan_decode_split_bf16(p, true));
+        *count = 1;
+        return SINKATTN_OK;
+    }
+    put_launch(launches[0], bf16 ? sinkattn::plan_decode_split_bf16(p, false) : sinkattn::plan_decode_split_f32(p));
+    *count = 1;
+    if (form == SINKATTN_PLAN_DECODE) {
+        sinkattn::DecodeMergeParams mp{};
+        mp.batch = p.batch * p.q_len;
+        mp.q_len = p.q_len;
+        mp.num_q_heads = p.num_q_heads;
+        mp.num_chunks = num_chunks;
+        put_launch(launches[1], sinkattn::plan_decode_merge(mp));
+        *count = 2;
+    }
+    return SINKATTN_OK;
+}
+
+sinkattn_status sinkattn_plan_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                      const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                      const sinkattn_tensor* cu_seqlens_q,
+                                      const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
+                                      int num_splits, sinkattn_launch* launches, int* count) {
+    g_last_error.clear();
+    if (launches == nullptr || count == nullptr) return fail(SINKATTN_ERR_NULL, "launches/count is NULL");
+    *count = 0;
+    sinkattn::PrefillParams p{};
+    SA_TRY(check_prefill_inputs(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, scale, causal, p));
+    if (num_splits < 0 || num_splits > 65536)
+        return fail(SINKATTN_ERR_SHAPE, "num_splits must be 0 (unsplit) or in [1, 65536] (got %d)", num_splits);
+    if (num_splits > 0 && p.total_q * p.num_q_heads * static_cast<int64_t>(num_splits) >= (int64_t(1) << 31))
+        return fail(SINKATTN_ERR_UNSUPPORTED, "Tq * Hq * num_splits too large");
+    if (p.total_q == 0 || p.num_seqs == 0) return SINKATTN_OK;
+    // The launchers tell the split form by a non-null partial_o; the plan only needs that bit.
+    static float split_marker;
+    if (num_splits > 0) {
+        p.num_splits = num_splits;
+        p.partial_o = &split_marker;
+    }
+    const sinkattn::Launch l =
+        q->dtype == SINKATTN_BF16 ? sinkattn::plan_prefill_bf16(p) : sinkattn::plan_prefill_f32(p);
+    if (l.grid > sinkattn::kMaxGrid) return fail(SINKATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    put_launch(launches[0], l);
+    *count = 1;
+    return SINKATTN_OK;
+}
 
 int sinkattn_version(void) { return SINKATTN_VERSION; }
 

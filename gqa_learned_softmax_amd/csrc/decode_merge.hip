@@ -8,13 +8,10 @@
 #include "chunk_merge.h"
 #include "device_common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace sinkattn {
 namespace {
-
-constexpr int kMergeWaves = 4;
-
-constexpr int64_t kRowsForX4 = 8192;
 
 // Four rows per wave (chunks <= 16). Rows past the end are clamped to the last row and not
 // written, so every lane stays active for the quarter reductions.
@@ -71,14 +68,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeMe
 }  // namespace
 
 hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream) {
-    const int64_t rows = static_cast<int64_t>(p.batch) * p.num_q_heads;
-    if (rows >= kRowsForX4 && p.num_chunks <= 16) {
-        const int64_t blocks = (rows + 4 * kMergeWaves - 1) / (4 * kMergeWaves);
-        decode_merge_x4_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kMergeWaves * 64), 0, stream>>>(p);
-        return hipGetLastError();
-    }
-    const int64_t blocks = (rows + kMergeWaves - 1) / kMergeWaves;
-    decode_merge_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kMergeWaves * 64), 0, stream>>>(p);
+    const Launch l = plan_decode_merge(p);
+    if (merge_four_rows_per_wave(p))
+        decode_merge_x4_kernel<<<dim3(static_cast<unsigned>(l.grid)), dim3(l.block), 0, stream>>>(p);
+    else
+        decode_merge_kernel<<<dim3(static_cast<unsigned>(l.grid)), dim3(l.block), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -40,12 +40,11 @@
 #include "chunk_merge.h"
 #include "device_common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace sinkattn {
 namespace {
 
-constexpr int kSplitWaves = 4;
-constexpr int kSplitThreads = kSplitWaves * 64;
 constexpr int kBlockKeys = 64;  // keys per staged block
 // K tile row pitch in bf16 elements: 144 bytes, so the 16-byte reads of 16 consecutive rows start
 // on 16 disjoint 4-bank groups.
@@ -543,50 +542,24 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(DecodeSplitParams
 
 }  // namespace
 
-// Compute units of an MI355X / MI350X (gfx950).
-constexpr int64_t kComputeUnits = 256;
-
-// Group adjacent KV heads per work-group where their slices of a cache row are adjacent
-// (token-major caches): the wider the contiguous piece of every row a work-group reads, the closer
-// the stream comes to the copy rate (measured on MI355X: one head 345 us, two 307 us, four 283 us
-// on 32 sequences of 16K-32K keys). Four heads (512 bytes of every row, 1024 threads, 152 KB of LDS,
-// one work-group per CU) when that still gives at least two rounds of work-groups; two heads when
-// the paired grid gives every compute unit a work-group; otherwise one. The host allows at most 64
-// query rows (four tiles) per KV head.
-struct SplitShape {
-    int heads;       // KV heads per work-group
-    int64_t groups;  // work-groups in the grid
-};
-
-SplitShape split_shape(const DecodeSplitParams& p) {
-    const bool adjacent = p.k_stride_head == kHeadDim && p.v_stride_head == kHeadDim;
-    const int64_t paired_groups = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 2) * p.num_chunks;
-    const int64_t quad_groups = static_cast<int64_t>(p.batch) * (p.num_kv_heads / 4) * p.num_chunks;
-    if (p.num_kv_heads % 4 == 0 && adjacent && quad_groups >= 2 * kComputeUnits) return {4, quad_groups};
-    if (p.num_kv_heads % 2 == 0 && adjacent && paired_groups >= kComputeUnits) return {2, paired_groups};
-    return {1, static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_chunks};
-}
-
-template <bool kFused, bool kKeySplit>
-hipError_t launch_split_as(const DecodeSplitParams& p, hipStream_t stream) {
-    const SplitShape shape = split_shape(p);
-    const dim3 grid(static_cast<unsigned>(shape.groups));
-    if (shape.heads == 4) {
-        decode_split_bf16_kernel<4, kFused, kKeySplit><<<grid, dim3(4 * kSplitThreads), 0, stream>>>(p);
-    } else if (shape.heads == 2) {
-        decode_split_bf16_kernel<2, kFused, kKeySplit><<<grid, dim3(2 * kSplitThreads), 0, stream>>>(p);
-    } else {
-        decode_split_bf16_kernel<1, kFused, kKeySplit><<<grid, dim3(kSplitThreads), 0, stream>>>(p);
-    }
+// Launches the kernel instance decode_shape (plan.h) names: KV heads per work-group, key split,
+// single launch or not.
+template <int kHeads, bool kFused>
+hipError_t launch_split_heads(const DecodeSplitParams& p, const DecodeShape& s, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(s.groups)), block(static_cast<unsigned>(s.block));
+    if (s.key_split)
+        decode_split_bf16_kernel<kHeads, kFused, true><<<grid, block, 0, stream>>>(p);
+    else
+        decode_split_bf16_kernel<kHeads, kFused, false><<<grid, block, 0, stream>>>(p);
     return hipGetLastError();
 }
 
-// With one column tile (G x T <= 16 query rows per KV head) the four waves of a KV head split the
-// keys of each block; with more, each wave folds one column tile over all keys.
 template <bool kFused>
 hipError_t launch_split(const DecodeSplitParams& p, hipStream_t stream) {
-    const int columns = p.num_q_heads / p.num_kv_heads * p.q_len;
-    return columns <= 16 ? launch_split_as<kFused, true>(p, stream) : launch_split_as<kFused, false>(p, stream);
+    const DecodeShape s = decode_shape(p);
+    if (s.heads == 4) return launch_split_heads<4, kFused>(p, s, stream);
+    if (s.heads == 2) return launch_split_heads<2, kFused>(p, s, stream);
+    return launch_split_heads<1, kFused>(p, s, stream);
 }
 
 hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stream) {
@@ -597,14 +570,9 @@ hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stre
     return launch_split<true>(p, stream);
 }
 
-bool decode_fused_fits_one_round(const DecodeSplitParams& p) {
-    return split_shape(p).groups <= kComputeUnits;
-}
-
 hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t stream) {
-    const int64_t total = static_cast<int64_t>(p.batch) * p.q_len * p.num_q_heads * p.num_chunks;
-    const int64_t blocks = (total + 255) / 256;
-    decode_split_f32_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(p);
+    const Launch l = plan_decode_split_f32(p);
+    decode_split_f32_kernel<<<dim3(static_cast<unsigned>(l.grid)), dim3(l.block), 0, stream>>>(p);
     return hipGetLastError();
 }
 

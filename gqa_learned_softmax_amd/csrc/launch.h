@@ -94,10 +94,6 @@ hipError_t launch_decode_split_bf16(const DecodeSplitParams& p, hipStream_t stre
 hipError_t launch_decode_split_f32(const DecodeSplitParams& p, hipStream_t stream);
 // Split and merge in one launch (bf16); partials and counters as in DecodeSplitParams.
 hipError_t launch_decode_fused_bf16(const DecodeSplitParams& p, hipStream_t stream);
-// True when the bf16 split grid has at most one work-group per compute unit. Only then does the
-// single launch pay: on a longer grid every work-group that finishes early holds its compute unit
-// through the arrival count and, for the last one, the merge, while split then merge does not.
-bool decode_fused_fits_one_round(const DecodeSplitParams& p);
 hipError_t launch_decode_merge(const DecodeMergeParams& p, hipStream_t stream);
 
 // sinkattn_decode_static: the library-owned workspace, one per GPU (static_workspace.hip).

@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace sinkattn {
 namespace {
@@ -41,10 +42,6 @@ namespace {
 // registers spilled to the stack.
 #define SA_INLINE __attribute__((always_inline))
 
-constexpr int kPfWaves = 4;
-constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kRowsPerWave = 64;                       // two 32-column MFMA blocks
-constexpr int kRowsPerTile = kPfWaves * kRowsPerWave;  // 256 query rows per work-group
 constexpr int kKeyTile = 64;
 // K and V tiles sit in LDS unpadded (64 keys x 128-byte rows) in three buffers, written straight
 // from global memory by buffer_load ... lds (no staging registers), one tile two tiles ahead of
@@ -770,26 +767,19 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
-    const int group = p.num_q_heads / p.num_kv_heads;
-    const int positions_per_tile = kRowsPerTile / group;
-    // Upper bound on query tiles without reading cu_seqlens: each sequence adds at most one
-    // partial tile beyond ceil(Tq / positions_per_tile).
-    const int64_t tiles = (p.total_q + positions_per_tile - 1) / positions_per_tile + p.num_seqs;
-    const bool split = p.partial_o != nullptr;
-    const int64_t blocks = tiles * p.num_kv_heads * (split ? p.num_splits : 1);
-    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
-    if (split)
-        prefill_bf16_kernel<true><<<dim3(static_cast<unsigned>(blocks)), dim3(kPfThreads), 0, stream>>>(p);
+    const Launch l = plan_prefill_bf16(p);
+    if (l.grid > kMaxGrid) return hipErrorInvalidConfiguration;
+    if (p.partial_o != nullptr)
+        prefill_bf16_kernel<true><<<dim3(static_cast<unsigned>(l.grid)), dim3(l.block), 0, stream>>>(p);
     else
-        prefill_bf16_kernel<false><<<dim3(static_cast<unsigned>(blocks)), dim3(kPfThreads), 0, stream>>>(p);
+        prefill_bf16_kernel<false><<<dim3(static_cast<unsigned>(l.grid)), dim3(l.block), 0, stream>>>(p);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t stream) {
-    const int64_t total = p.total_q * p.num_q_heads;
-    const int64_t blocks = (total + 255) / 256;
-    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
-    prefill_f32_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(p);
+    const Launch l = plan_prefill_f32(p);
+    if (l.grid > kMaxGrid) return hipErrorInvalidConfiguration;
+    prefill_f32_kernel<<<dim3(static_cast<unsigned>(l.grid)), dim3(l.block), 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_VERSION 6
+#define SINKATTN_VERSION 7
 
 typedef enum {
     SINKATTN_OK = 0,
@@ -72,7 +72,7 @@ typedef enum {
 /* A strided view of device memory. Only the first `ndim` entries of shape/stride are read. */
 typedef struct {
     void* data;          /* device pointer (caller-owned) */
-    sinkattn_dtype dtype;
+    int32_t dtype;       /* a sinkattn_dtype value; any other value is rejected (SINKATTN_ERR_DTYPE) */
     int32_t ndim;        /* 1..4 */
     int64_t shape[4];    /* extents, >= 0 */
     int64_t stride[4];   /* in elements */
@@ -367,6 +367,51 @@ sinkattn_status sinkattn_linear_fp8_block_scaled(const sinkattn_tensor* x, const
                                                  const sinkattn_tensor* w, const sinkattn_tensor* scale_w,
                                                  const sinkattn_tensor* bias, const sinkattn_tensor* y,
                                                  void* stream);
+/* ---------------------------------------------------------------------------------------------
+ * Launch plans: the kernels a call launches for given inputs, reported without launching.
+ *
+ * For profilers and reports (which kernel of a profile belongs to which call) and for checking
+ * the grid choice on a machine without a GPU. The inputs are validated exactly as the call itself
+ * validates them (same status and sinkattn_last_error text on rejection); their data pointers are
+ * checked for alignment only and never dereferenced, so host addresses or placeholders of the
+ * right alignment do. Nothing is launched, allocated or synchronised.
+ *
+ *   kernel   the kernel's name as a profiler prints it, without namespace or parameter list
+ *            (template arguments included, e.g. "decode_split_bf16_kernel<2, false, true>")
+ *   grid     work-groups of the launch
+ *   block    threads per work-group
+ */
+typedef struct {
+    char kernel[96];
+    int64_t grid;
+    int32_t block;
+} sinkattn_launch;
+
+/* Which call of the decode family to plan (the `form` argument of sinkattn_plan_decode). */
+typedef enum {
+    SINKATTN_PLAN_DECODE_SPLIT = 0, /* sinkattn_decode_split (q rank 3) / _multi_split (q rank 4) */
+    SINKATTN_PLAN_DECODE = 1        /* sinkattn_decode / _multi / _static (same kernels) */
+} sinkattn_plan_form;
+
+/* Plans of the decode family for q [B, Hq, D] or [B, T, Hq, D], k/v, sinks, seqlens_k, num_chunks
+ * and scale as in those calls. Writes the launches in launch order to launches[0 .. *count - 1]:
+ * one for the split form; for sinkattn_decode one (split and merge in a single launch) or two
+ * (split, then merge); none when B = 0 or T = 0. `launches` must have room for two entries.
+ * Section "Kernels for GPT-OSS", subsection "Sink attention", of "GPT-OSS on Day 0" (the
+ * split-KV decode these kernels carry out). */
+sinkattn_status sinkattn_plan_decode(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                     const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                     const sinkattn_tensor* seqlens_k, int num_chunks, float scale,
+                                     int form, sinkattn_launch* launches, int* count);
+
+/* Plan of sinkattn_prefill (num_splits = 0) or sinkattn_prefill_split (num_splits >= 1) for
+ * these inputs: one launch in launches[0], none when Tq = 0 or B = 0. */
+sinkattn_status sinkattn_plan_prefill(const sinkattn_tensor* q, const sinkattn_tensor* k,
+                                      const sinkattn_tensor* v, const sinkattn_tensor* sinks,
+                                      const sinkattn_tensor* cu_seqlens_q,
+                                      const sinkattn_tensor* cu_seqlens_k, float scale, int causal,
+                                      int num_splits, sinkattn_launch* launches, int* count);
+
 /* Short static description of a status code. Never NULL. */
 const char* sinkattn_status_string(sinkattn_status status);
 

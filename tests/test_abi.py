@@ -60,7 +60,7 @@ def test_every_declared_function_is_exported():
 
 
 CEILINGS_HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sinkattn_ceilings.h")
-CEILINGS_LIB = os.path.join(os.path.dirname(_lib.LIB_PATH), "libsinkattn_ceilings.so")
+CEILINGS_LIB = os.path.join(os.path.dirname(_lib.DEFAULT_LIB_PATH), "libsinkattn_ceilings.so")
 
 
 def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():

@@ -5,7 +5,8 @@ Both sides see the same seeded inputs (bf16 values upcast exactly for the oracle
   all compared output elements;
 * fp32 reference variant: ||gpu - oracle||_inf / ||oracle||_inf <= 1e-5.
 Small cases compare every output element; the full-size workloads compare every output where the
-oracle is cheap (decode) and sampled (token, head) rows otherwise (prefill).
+oracle is cheap (decode, the long decode included) and, for prefill, every work-group tile's first
+and last query position for every KV group plus random (token, head) rows.
 """
 from __future__ import annotations
 
@@ -379,49 +380,74 @@ def test_full_decode_workload_2():
 
 
 def _decode_rows(case, pairs):
-    """Oracle decode for selected (b, kv-head) groups; returns {(b, g): out [G, D]}."""
+    """Oracle decode for selected (b, kv-head) groups; returns {(b, g): (out [G, D], lse [G])}."""
     group = case.q.shape[1] // case.k.shape[2]
     res = {}
     for b, g in pairs:
         q = _np(case.q[b:b + 1, g * group:(g + 1) * group])
         n = int(case.seqlens_k[b])
-        k = _np32(case.k[b:b + 1, :n, g:g + 1])
-        v = _np32(case.v[b:b + 1, :n, g:g + 1])
-        out, _ = oracle.decode(q, k, v, _np(case.sinks[g * group:(g + 1) * group]), [n], case.scale)
-        res[(b, g)] = out[0]
+        k = _np(case.k[b:b + 1, :n, g:g + 1])
+        v = _np(case.v[b:b + 1, :n, g:g + 1])
+        out, lse = oracle.decode(q, k, v, _np(case.sinks[g * group:(g + 1) * group]), [n], case.scale)
+        res[(b, g)] = (out[0], lse[0])
     return res
 
 
-def test_full_long_decode_workload_4_sampled():
+def test_full_long_decode_workload_4_all_groups():
+    """Every (sequence, KV-head) group of the long decode: all 32 x 8 groups, output and lse."""
     sa = _sa()
     case = workloads.make(4, poison=True).decode
-    _, _, _, out, _ = run_decode(sa, case, return_lse=False)
-    rng = np.random.default_rng(4)
-    pairs = {(int(b), int(g)) for b, g in zip(rng.integers(0, 32, 24), rng.integers(0, 8, 24))}
-    pairs |= {(0, 0), (31, 7)}
-    ref = _decode_rows(case, sorted(pairs))
-    group = 8
-    g_out = np.stack([_np(out[b, g * group:(g + 1) * group]) for b, g in sorted(pairs)])
-    r_out = np.stack([ref[p] for p in sorted(pairs)])
-    check_bf16(torch.from_numpy(g_out), r_out, "workload 4 decode (sampled groups)")
+    _, _, _, out, lse = run_decode(sa, case)
+    pairs = [(b, g) for b in range(case.q.shape[0]) for g in range(case.k.shape[2])]
+    ref = _decode_rows(case, pairs)
+    group = case.q.shape[1] // case.k.shape[2]
+    g_out = np.stack([_np(out[b, g * group:(g + 1) * group]) for b, g in pairs])
+    r_out = np.stack([ref[p][0] for p in pairs])
+    check_bf16(torch.from_numpy(g_out), r_out, "workload 4 decode (all 256 groups)")
+    g_lse = np.stack([_np(lse[b, g * group:(g + 1) * group]) for b, g in pairs])
+    r_lse = np.stack([ref[p][1] for p in pairs])
+    np.testing.assert_allclose(g_lse, r_lse, atol=1e-3)
 
 
-def _sampled_prefill(sa, case, n_samples, seed, label):
-    out = run_prefill(sa, case)
+def _stratified_rows(case, n_random, seed):
+    """(token, head) rows to check at full size: for every work-group query tile (32 consecutive
+    positions of one sequence, which the kernel runs for the 8 heads of one KV group) its first
+    and its last position, once for each KV group, the head within the group rotating from tile
+    to tile; plus ``n_random`` uniformly drawn rows. That reaches every tile, the diagonal tiles
+    where the causal mask cuts through, and every tile's first and last wave."""
+    tile_positions = 32
+    h_q, h_kv = case.q.shape[1], case.k.shape[1]
+    group = h_q // h_kv
+    tokens, heads = [], []
+    cu = case.cu_seqlens_q.tolist()
+    tile_index = 0
+    for b in range(len(cu) - 1):
+        for start in range(cu[b], cu[b + 1], tile_positions):
+            last = min(start + tile_positions, cu[b + 1]) - 1
+            for j, t in enumerate((start, last)):
+                for g in range(h_kv):
+                    tokens.append(t)
+                    heads.append(g * group + (tile_index + 3 * j + g) % group)
+            tile_index += 1
     rng = np.random.default_rng(seed)
-    t_q = case.q.shape[0]
-    tokens = np.concatenate([rng.integers(0, t_q, n_samples), [0, t_q - 1]])
-    heads = np.concatenate([rng.integers(0, case.q.shape[1], n_samples), [0, case.q.shape[1] - 1]])
-    ref, _ = oracle.prefill_at(_np32(case.q), _np32(case.k), _np32(case.v), _np(case.sinks), case.cu_seqlens_q.numpy(),
+    tokens += rng.integers(0, case.q.shape[0], n_random).tolist()
+    heads += rng.integers(0, h_q, n_random).tolist()
+    return np.array(tokens), np.array(heads)
+
+
+def _stratified_prefill(sa, case, n_random, seed, label):
+    out = run_prefill(sa, case)
+    tokens, heads = _stratified_rows(case, n_random, seed)
+    ref, _ = oracle.prefill_at(_np(case.q), _np(case.k), _np(case.v), _np(case.sinks), case.cu_seqlens_q.numpy(),
                                case.cu_seqlens_k.numpy(), case.scale, case.causal, tokens, heads)
     g = out[torch.from_numpy(tokens).cuda(), torch.from_numpy(heads).cuda()]
-    check_bf16(g, ref, label)
+    check_bf16(g, ref, f"{label} ({len(tokens)} rows)")
 
 
-def test_full_prefill_workload_3_sampled():
+def test_full_prefill_workload_3_stratified():
     sa = _sa()
     case = workloads.make(3).prefill
-    _sampled_prefill(sa, case, 400, 3, "workload 3 prefill (sampled rows)")
+    _stratified_prefill(sa, case, 400, 3, "workload 3 prefill (every tile's first and last row)")
 
 
 def test_full_mixed_workload_5():
@@ -430,7 +456,7 @@ def test_full_mixed_workload_5():
     po, pm, pd, out, lse = run_decode(sa, w.decode)
     ref, rlse = oracle_decode(w.decode)
     check_bf16(out, ref, "workload 5 decode")
-    _sampled_prefill(sa, w.prefill, 400, 5, "workload 5 prefill (sampled rows)")
+    _stratified_prefill(sa, w.prefill, 400, 5, "workload 5 prefill (every tile's first and last row)")
 
 
 def test_graph_replays_match_eager():

@@ -188,6 +188,21 @@ __device__ __forceinline__ void stage_store(const KvStage& r, __bf16 (*kt)[kBloc
     }
 }
 
+// SINKATTN_POISON_LDS builds: NaN into exactly the elements stage_store writes for this thread.
+template <int kHeads>
+__device__ __forceinline__ void stage_poison(__bf16 (*kt)[kBlockKeys][kKPitch], __bf16 (*vt)[kBlockKeys][kVPitch],
+                                             int tid) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int piece = tid + j * kSplitThreads * kHeads;
+        const int row = piece / (8 * kHeads);
+        const int hh = (piece / 8) % kHeads;
+        const int seg = piece % 8;
+        *reinterpret_cast<bf16x8*>(&kt[hh][row][8 * seg]) = nan_bf16x8();
+        *reinterpret_cast<bf16x8*>(&vt[hh][row][8 * seg]) = nan_bf16x8();
+    }
+}
+
 // One wave, one column tile, one staged block: S^T from the K tile (lane (col, grp) reads key row
 // 16t + col, elements 8grp and 32 + 8grp: the A operands of the 16x16x32 products), the online
 // softmax, and O^T += V^T . P^T with V^T from transpose reads of the V tile: lane (grp, col) points
@@ -318,9 +333,9 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     // Every wave covers the whole chunk for its columns, so each starts chunk 0 from the sink; with
     // the key split the waves hold parts of one state, and only wave 0 carries the sink.
     float m = kNegInf, dsum = 0.0f;
-    if (chunk == 0 && (!kKeySplit || tile == 0)) {
+    if ((chunk == 0 || kMutateSinkEveryChunk) && (!kKeySplit || tile == 0)) {
         m = p.sinks[head] * kLog2e;
-        dsum = (grp == 0 && m != kNegInf) ? 1.0f : 0.0f;
+        dsum = (grp == 0 && m != kNegInf && !kMutateD0Zero) ? 1.0f : 0.0f;
     }
     f32x4 acc[4];
 #pragma unroll
@@ -338,6 +353,13 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
 
     const int blocks = hi > lo ? static_cast<int>((hi - lo + kBlockKeys - 1) / kBlockKeys) : 0;
     const uint32_t base0 = static_cast<uint32_t>(lo);
+    if constexpr (kPoisonLds) {
+        bf16x8* kz = reinterpret_cast<bf16x8*>(&k_lds[0][0][0][0]);
+        bf16x8* vz = reinterpret_cast<bf16x8*>(&v_lds[0][0][0][0]);
+        for (int i = tid; i < static_cast<int>(sizeof(k_lds) / 16); i += kSplitThreads * kHeads) kz[i] = nan_bf16x8();
+        for (int i = tid; i < static_cast<int>(sizeof(v_lds) / 16); i += kSplitThreads * kHeads) vz[i] = nan_bf16x8();
+        __syncthreads();
+    }
     KvStage ra, rb;
     stage_load<kHeads>(ra, krs, vrs, k_row_bytes, v_row_bytes, base0, tid);
     stage_store<kHeads>(ra, k_lds[0], v_lds[0], tid);
@@ -346,6 +368,7 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     // Blocks past the chunk end load as zeros without touching memory; the loop stops before
     // folding them.
     for (int i = 0; i < blocks;) {
+        if constexpr (kPoisonLds) stage_poison<kHeads>(k_lds[(i + 1) & 1], v_lds[(i + 1) & 1], tid);
         stage_load<kHeads>(rb, krs, vrs, k_row_bytes, v_row_bytes, base0 + kBlockKeys * (i + 2), tid);
         if constexpr (kKeySplit)
             fold_keys(m, dsum, acc, k_lds[i & 1][hsub], v_lds[i & 1][hsub], q_op,
@@ -356,6 +379,7 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
         stage_store<kHeads>(ra, k_lds[(i + 1) & 1], v_lds[(i + 1) & 1], tid);
         __syncthreads();
         if (++i >= blocks) break;
+        if constexpr (kPoisonLds) stage_poison<kHeads>(k_lds[(i + 1) & 1], v_lds[(i + 1) & 1], tid);
         stage_load<kHeads>(ra, krs, vrs, k_row_bytes, v_row_bytes, base0 + kBlockKeys * (i + 2), tid);
         if constexpr (kKeySplit)
             fold_keys(m, dsum, acc, k_lds[i & 1][hsub], v_lds[i & 1][hsub], q_op,
@@ -510,9 +534,9 @@ __global__ __launch_bounds__(256) void decode_split_f32_kernel(DecodeSplitParams
         acc[d] = 0.0f;
     }
     float m = kNegInf, dsum = 0.0f;
-    if (chunk == 0) {
+    if (chunk == 0 || kMutateSinkEveryChunk) {
         m = p.sinks[head];
-        dsum = m == kNegInf ? 0.0f : 1.0f;
+        dsum = (m == kNegInf || kMutateD0Zero) ? 0.0f : 1.0f;
     }
     const float* kb = static_cast<const float*>(p.k) + b * p.k_stride_b + g * p.k_stride_head;
     const float* vb = static_cast<const float*>(p.v) + b * p.v_stride_b + g * p.v_stride_head;

@@ -12,6 +12,30 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Debug builds only; the shipped library defines none of these.
+//  SINKATTN_POISON_LDS: every LDS staging buffer is filled with NaN before each refill (and once at
+//    the start), so a read that races its refill, or reads a part no refill writes, puts NaN into
+//    the output instead of going unnoticed with stale values.
+//  SINKATTN_MUTATE_SINK_EVERY_CHUNK: every KV chunk (decode) and split (prefill) starts from the
+//    sink, not only the first one -- a deliberate mistake the parity tests must catch.
+//  SINKATTN_MUTATE_D0_ZERO: rows start at m = sink with d = 0, so the sink sets the starting
+//    reference but adds nothing to the denominator -- likewise a deliberate mistake.
+#ifdef SINKATTN_POISON_LDS
+constexpr bool kPoisonLds = true;
+#else
+constexpr bool kPoisonLds = false;
+#endif
+#ifdef SINKATTN_MUTATE_SINK_EVERY_CHUNK
+constexpr bool kMutateSinkEveryChunk = true;
+#else
+constexpr bool kMutateSinkEveryChunk = false;
+#endif
+#ifdef SINKATTN_MUTATE_D0_ZERO
+constexpr bool kMutateD0Zero = true;
+#else
+constexpr bool kMutateD0Zero = false;
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
@@ -97,6 +121,13 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
     return z;
+}
+
+// Eight bf16 quiet NaNs (bit pattern 0x7FC0), the poison of SINKATTN_POISON_LDS builds.
+__device__ __forceinline__ bf16x8 nan_bf16x8() {
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    const u16x8 bits = {0x7FC0, 0x7FC0, 0x7FC0, 0x7FC0, 0x7FC0, 0x7FC0, 0x7FC0, 0x7FC0};
+    return __builtin_bit_cast(bf16x8, bits);
 }
 
 __device__ __forceinline__ f32x4 zero_f32x4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }

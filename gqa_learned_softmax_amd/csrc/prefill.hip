@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         // clamped to Lk, which may fall inside a tile) processes no tile at all.
         kt_begin = lo / kKeyTile;
         kt_end = hi > lo ? max(kt_begin, min(num_tiles, (hi + kKeyTile - 1) / kKeyTile)) : kt_begin;
-        carries_sink = split == 0;
+        carries_sink = split == 0 || kMutateSinkEveryChunk;
     }
 
     // K/V rows [0, key_end) of KV head g of this sequence; loads past the end return zeros.
@@ -201,6 +201,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         const int b = kt % kStages;
         const uint32_t k_soff = static_cast<uint32_t>(kt * kKeyTile) * k_row_bytes;
         const uint32_t v_soff = static_cast<uint32_t>(kt * kKeyTile) * v_row_bytes;
+        if constexpr (kPoisonLds) {
+            // NaN into the 16 bytes each load below will write (lane l: byte 16 l of the wave's
+            // 1 KB), complete before the loads are issued.
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                *reinterpret_cast<bf16x8*>(&k_lds[b][(16 * wave + 8 * j) * 64 + 8 * lane]) = nan_bf16x8();
+                *reinterpret_cast<bf16x8*>(&v_lds[b][(16 * wave + 8 * j) * 64 + 8 * lane]) = nan_bf16x8();
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t k_dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -569,9 +579,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
             // condition the switch after a running-max tile checks, so even the first tile can
             // run without row maxima.
             m[cb] = carries_sink ? sink2[cb] : kNegInf;
-            dsum[cb] = (half == 0 && m[cb] != kNegInf) ? 1.0f : 0.0f;
+            dsum[cb] = (half == 0 && m[cb] != kNegInf && !kMutateD0Zero) ? 1.0f : 0.0f;
             if (kAllowFast && m[cb] >= -kZeroRefLimit && m[cb] <= kZeroRefLimit) {
-                dsum[cb] = half == 0 ? exp2_fast(m[cb]) : 0.0f;
+                dsum[cb] = (half == 0 && !kMutateD0Zero) ? exp2_fast(m[cb]) : 0.0f;
                 m[cb] = 0.0f;
             }
 #pragma unroll
@@ -626,6 +636,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 #pragma unroll
             for (int r = 0; r < 16; ++r) bad |= !__builtin_isfinite(acc[cb][n][r]);
     }
+    // Poisoned-LDS builds never start again: a NaN read from a poisoned buffer must reach the
+    // output rather than be recomputed (they are run on inputs that need no second pass).
+    if constexpr (kPoisonLds) bad = false;
     if (tid == 0) redo_general = 0;
     __syncthreads();
     if (__any(bad) && lane == 0) redo_general = 1;
@@ -736,7 +749,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
     };
     auto start = [&](bool with_sink) {
         m = with_sink ? p.sinks[head] : kNegInf;
-        dsum = m == kNegInf ? 0.0f : 1.0f;
+        dsum = (m == kNegInf || kMutateD0Zero) ? 0.0f : 1.0f;
         for (int d = 0; d < kHeadDim; ++d) acc[d] = 0.0f;
     };
     if (p.partial_o != nullptr) {
@@ -746,7 +759,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillParams p) {
         for (int sp = 0; sp < p.num_splits; ++sp) {
             const int lo = min(sp * split_keys, k_len);
             const int hi = min(lo + split_keys, key_end);
-            start(sp == 0);
+            start(sp == 0 || kMutateSinkEveryChunk);
             fold(lo, hi);
             const int64_t row = (static_cast<int64_t>(tok) * p.num_q_heads + head) * p.num_splits + sp;
             const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;

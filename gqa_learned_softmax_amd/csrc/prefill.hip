@@ -452,9 +452,14 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
             acc[j >> 1][j & 1] = mfma32x32x16(vo[j & 1], (j >> 1) ? fp1[u] : fp0[u], acc[j >> 1][j & 1]);
     };
     auto row_sum = [&](int cb, const bf16x8& pt) SA_INLINE { rsum[cb] = mfma16x16x32(rsum_sel, pt, rsum[cb]); };
-    auto fast_tile = [&](int kt, auto carry_tag) SA_INLINE {
+    // buf_tag: the tile's LDS buffer (kt % 3) as a compile-time constant, or -1 to compute it. With a
+    // constant buffer every LDS read folds the buffer into its immediate offset; computed, each
+    // read's lane address needs a vector add per tile.
+    auto fast_tile = [&](int kt, auto carry_tag, auto buf_tag) SA_INLINE {
         constexpr bool kCarry = decltype(carry_tag)::value;
-        const int buf = kt % kStages;
+        constexpr int kBuf = decltype(buf_tag)::value;
+        const int buf = kBuf >= 0 ? kBuf : kt % kStages;
+        const int next_buf = kBuf >= 0 ? (kBuf + 1) % kStages : (kt + 1) % kStages;
         const __bf16* kt_lds = k_lds[buf];
         const __bf16* vt_lds = v_lds[buf];
         bf16x8 k1[4], va[2], vb[2];
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         SA_SLOT_END();
         // t8: PV1 | E01b; V^T of k-step 3 (carried); K of the next tile's first key half
         v_step(vt_lds, 3, vcarry[1]);
-        k_half(k_lds[(kt + 1) % kStages], 0, kpre);
+        k_half(k_lds[next_buf], 0, kpre);
         pv_step(vb, 1);
         row_sum(0, fp0[2]);
         exp_regs(fs01, 0.0f, true, fp0, 1, 8, 8, no_sum, no_sum, false);
@@ -610,8 +615,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
             if (kt < unmasked_end) {
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb) rsum[cb] = zero_f32x4();
-                fast_tile(kt++, False());
-                for (; kt < unmasked_end; ++kt) fast_tile(kt, True());
+                using Computed = std::integral_constant<int, -1>;
+                fast_tile(kt++, False(), Computed());
+                // Up to buffer 0, then three tiles at a time with their buffers known at compile
+                // time, then the remainder.
+                for (; kt < unmasked_end && kt % kStages != 0; ++kt) fast_tile(kt, True(), Computed());
+                for (; kt + kStages <= unmasked_end; kt += kStages) {
+                    fast_tile(kt, True(), std::integral_constant<int, 0>());
+                    fast_tile(kt + 1, True(), std::integral_constant<int, 1>());
+                    fast_tile(kt + 2, True(), std::integral_constant<int, 2>());
+                }
+                for (; kt < unmasked_end; ++kt) fast_tile(kt, True(), Computed());
                 drain_fast();
             }
             for (; kt < kt_end; ++kt) plain_tile(kt, True(), True(), False());

@@ -191,16 +191,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
         dma_k_off[j] = row * k_row_bytes + 16 * (pos ^ ((row >> 1) & 7));
         dma_v_off[j] = row * v_row_bytes + 16 * (pos ^ (((row >> 1) & 1) << 2));
     }
-    // Issues the loads of KV tile kt into buffer kt % 3 (tiles past the end load zeros): 16 bytes
+    // Issues the loads of KV tile kt into buffer kt % 3 (rows past the end load zeros): 16 bytes
     // a lane straight into LDS (buffer_load ... lds; M0 holds the LDS address of the wave's 1 KB).
+    // The whole byte offset goes in the lane's offset register: the buffer range check covers that
+    // register (and the instruction offset) but not the scalar offset, so rows past the end read
+    // zeros instead of whatever memory follows the tensor.
     // Written as inline asm: the compiler does not see LDS writes in flight that it cannot tell
     // apart from the buffers being read, and would otherwise wait for these loads before every
     // LDS read, which makes them synchronous. Their completion is waited for explicitly (vmcnt)
     // before each barrier. They have no destination registers; the asm reads its operands at issue.
     auto dma = [&](int kt) SA_INLINE {
         const int b = kt % kStages;
-        const uint32_t k_soff = static_cast<uint32_t>(kt * kKeyTile) * k_row_bytes;
-        const uint32_t v_soff = static_cast<uint32_t>(kt * kKeyTile) * v_row_bytes;
+        const uint32_t k_tile_off = static_cast<uint32_t>(kt * kKeyTile) * k_row_bytes;
+        const uint32_t v_tile_off = static_cast<uint32_t>(kt * kKeyTile) * v_row_bytes;
         if constexpr (kPoisonLds) {
             // NaN into the 16 bytes each load below will write (lane l: byte 16 l of the wave's
             // 1 KB), complete before the loads are issued.
@@ -220,16 +223,16 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
             asm volatile(
                 "s_mov_b32 m0, %0\n\t"
                 "s_nop 0\n\t"
-                "buffer_load_dwordx4 %1, %2, %3 offen lds"
+                "buffer_load_dwordx4 %1, %2, 0 offen lds"
                 :
-                : "s"(k_dst), "v"(dma_k_off[j]), "s"(krs), "s"(k_soff)
+                : "s"(k_dst), "v"(dma_k_off[j] + k_tile_off), "s"(krs)
                 : "memory", "m0");
             asm volatile(
                 "s_mov_b32 m0, %0\n\t"
                 "s_nop 0\n\t"
-                "buffer_load_dwordx4 %1, %2, %3 offen lds"
+                "buffer_load_dwordx4 %1, %2, 0 offen lds"
                 :
-                : "s"(v_dst), "v"(dma_v_off[j]), "s"(vrs), "s"(v_soff)
+                : "s"(v_dst), "v"(dma_v_off[j] + v_tile_off), "s"(vrs)
                 : "memory", "m0");
         }
     };

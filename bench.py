@@ -54,7 +54,7 @@ CALIB_BYTES = 256 * 2**20
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_b8_len8192_pmc.txt")
 # The split kernel's complete source: its traffic figure is only reused while these are unchanged.
 SPLIT_SOURCES = [os.path.join(ROOT, "gqa_learned_softmax_amd", "csrc", f)
-                 for f in ("decode_split.hip", "chunk_merge.h", "device_common.h", "launch.h")]
+                 for f in ("decode_split.hip", "chunk_merge.h", "device_common.h", "launch.h", "plan.h")]
 
 
 def _log(msg):

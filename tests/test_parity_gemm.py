@@ -6,9 +6,10 @@ bias term that starts the matrix-core accumulators ("GPT-OSS on Hopper"; "Kernel
 Bar, derived from the arithmetic: |gpu - oracle| <= u_out |oracle| + (K + 2 K/128) u_acc S per
 element, where u_out is the output rounding (2^-8 for bf16, 2^-24 for fp32), S the sum over k of
 |terms| (scales included) and u_acc the unit of one fp32 accumulation step - the worst-case bound
-of fp32 accumulation. u_acc = 2^-24 (round to nearest) for the bf16 products; 2^-23 for FP8, whose
-matrix instruction sums its 64 products with an internal rounding the ISA does not pin to
-round-to-nearest (measured errors exceed the 2^-24 bound by up to 1.3x, never the 2^-23 one). As a
+of fp32 accumulation. u_acc = 2^-24 (round to nearest) for the bf16 products; 2^-23 for FP8: the
+matrix instruction sums its 64 FP8 products internally in a rounding we cannot pin, and 2^-23 is the
+unit that holds for any faithful rounding of each step (error below one ulp, truncation included).
+Measured errors exceed the round-to-nearest 2^-24 bound by up to 1.3x and never the 2^-23 one. As a
 sharper check the mean error relative to S stays below 2^-9 (a wrong operand layout gives errors of
 order S).
 """

@@ -402,6 +402,14 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / n_rep
+    # The single launch, launched eagerly the same way (one Python call per step instead of two).
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n_rep):
+        fused(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_fused_eager = e0.elapsed_time(e1) / n_rep
     value = step_bytes / (ms_step * 1e-3) / 1e9
     fused_gbs = step_bytes / (ms_fused * 1e-3) / 1e9
     split_gbs = split_bytes / (ms_split * 1e-3) / 1e9
@@ -457,6 +465,7 @@ def main():
             "step_us_rotated": round(ms_step * 1e3, 3),
             "step_us_hot": round(ms_hot * 1e3, 3) if ms_hot else None,
             "step_us_eager_python_launch": round(ms_eager * 1e3, 3),
+            "fused_us_eager_python_launch": round(ms_fused_eager * 1e3, 3),
             "timing": "HIP graph replay of back-to-back calls, events on the replay stream",
             "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
             "step_frac_of_measured_stream_read": (round(value / ceilings["stream_read_128MiB_gbs"], 4)

@@ -7,66 +7,51 @@
 // every 32x32 accumulator block starts at the bias: a lane's 16 accumulators share one output
 // column (the MFMA C layout), so the bias costs one load per lane and block and no epilogue pass.
 //
-// Work-group: a 128 x 128 output tile, four waves of 64 x 64 (2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16, or of v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales for FP8).
-// Each K step stages 128 bytes of every A and B row (64 bf16 or 128 FP8 values = one scale block)
-// in double-buffered LDS tiles of pitch 144 bytes (16-byte reads of 16 consecutive rows hit disjoint
-// banks); the next step's loads are in flight while the current one is multiplied. FP8: each
-// 128-wide k block is multiplied into a temporary accumulator, then added to the running one times
-// scale_x[row, kb] * scale_w[column block, kb] (rows' scales staged in LDS with the tile).
+// Work-groups: 256 x 256 output tiles of eight waves of 128 x 64 (4 x 2 blocks, two waves per SIMD)
+// for bf16 problems large enough to fill the chip with them, else 128 x 128 tiles of four waves of
+// 64 x 64 (2 x 2 blocks, two work-groups per CU); FP8 always the latter. Blocks are
+// v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales for FP8.
+// Each K step's 128 bytes of every X and W row (64 bf16 or 128 FP8 values = one scale block) go
+// from memory straight into LDS with buffer_load ... lds, into two unpadded, swizzled stages; the
+// next step's loads are in flight while the current one is multiplied. FP8: each 128-wide k block
+// is multiplied into a temporary accumulator, then added to the running one times
+// scale_x[row, kb] * scale_w[column block, kb] (rows' scales staged in LDS beside each stage).
 // Tiles are spread XCD-aware: each XCD takes a contiguous range of tile indices, walked in groups of
 // 8 tile-rows so the X and W panels a group shares stay in that XCD's L2.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch_ops.h"
 
+// The kernels' lambdas are inlined by force: an outlined body becomes a call with its registers
+// spilled to the stack.
+#define SA_GEMM_INLINE __attribute__((always_inline))
+
 namespace sinkattn {
 namespace {
 
-constexpr int kStepBytes = 128;    // bytes of each row staged per K step
-constexpr int kRowPitch = 144;     // LDS row pitch in bytes
+constexpr int kStepBytes = 128;    // bytes of each row staged per K step (one LDS row)
 constexpr int kGroupRows = 8;      // tile-rows per group in the tile order
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Work-group layout: kWM x kWN waves, each owning kBM x kBN blocks of 32 x 32, so the tile is
-// (32 kBM kWM) x (32 kBN kWN). A step stages 8 sixteen-byte pieces per tile row.
+// (32 kBM kWM) x (32 kBN kWN).
 template <int kBM, int kBN, int kWM, int kWN>
 struct GemmShape {
     static constexpr int kThreads = 64 * kWM * kWN;
     static constexpr int kTileM = 32 * kBM * kWM;
     static constexpr int kTileN = 32 * kBN * kWN;
-    static constexpr int kPiecesA = kTileM * 8 / kThreads;
-    static constexpr int kPiecesB = kTileN * 8 / kThreads;
-    static_assert(kTileM * 8 % kThreads == 0 && kTileN * 8 % kThreads == 0, "whole pieces per thread");
     static_assert(kThreads >= kTileM, "one row scale per thread");
     static_assert(kTileN % 128 == 0 && 128 % (32 * kBN) == 0, "a wave's columns share one weight scale");
 };
 
-template <class S>
-struct GemmStage {
-    i32x4 a[S::kPiecesA];
-    i32x4 b[S::kPiecesB];
-    float sx;  // FP8: the scale of tile row tid (threads below the tile's row count)
-};
-
-template <bool kFp8, int kBM, int kBN, int kWM, int kWN>
-__global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_bias_kernel(GemmParams p) {
-    using S = GemmShape<kBM, kBN, kWM, kWN>;
-    constexpr int kThreads = S::kThreads, kTileM = S::kTileM, kTileN = S::kTileN;
-    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileM][kRowPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kTileN][kRowPitch];
-    __shared__ __attribute__((aligned(16))) float sx_lds[2][kTileM];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / kWN, wn = wave % kWN;
-    const int r32 = lane & 31, h = lane >> 5;
-
-    // Tile order: contiguous ranges per XCD (work-groups go round-robin over the 8 XCDs), grouped.
-    const int tiles_m = (p.m + kTileM - 1) / kTileM;
-    const int tiles_n = (p.n + kTileN - 1) / kTileN;
+// Output tile of this work-group. Tile order: contiguous ranges per XCD (work-groups go
+// round-robin over the 8 XCDs), walked in groups of kGroupRows tile-rows.
+__device__ __forceinline__ void tile_origin(const GemmParams& p, int tile_m, int tile_n, int& m0, int& n0) {
+    const int tiles_m = (p.m + tile_m - 1) / tile_m;
+    const int tiles_n = (p.n + tile_n - 1) / tile_n;
     const int tiles = tiles_m * tiles_n;
     int t = blockIdx.x;
     if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
@@ -75,9 +60,35 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
     const int group_rows = tiles_m - first_m < kGroupRows ? tiles_m - first_m : kGroupRows;
     const int tm = first_m + (t % per_group) % group_rows;
     const int tn = (t % per_group) / group_rows;
-    const int m0 = tm * kTileM, n0 = tn * kTileN;
+    m0 = tm * tile_m;
+    n0 = tn * tile_n;
+}
 
-    // Operand slices of this work-group; rows past M or N load as zeros (buffer range).
+// Each K step's 128 bytes of every X and W row go from memory straight into LDS (no staging
+// registers, no LDS store instructions: measured 4-15% faster than staging through registers, and
+// the freed registers are what let the eight-wave tile keep all its accumulators), two stages,
+// the loads of step i + 1 in flight while step i is multiplied, one barrier per step.
+// LDS rows are unpadded 128 bytes with 16-byte chunk c of row r at position c ^ ((r >> 1) & 7), so
+// the operand reads of 16 consecutive rows hit distinct banks; a load instruction fills 8 rows.
+template <bool kFp8, int kBM, int kBN, int kWM, int kWN>
+__global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_bias_dma_kernel(GemmParams p) {
+    using S = GemmShape<kBM, kBN, kWM, kWN>;
+    constexpr int kThreads = S::kThreads, kTileM = S::kTileM, kTileN = S::kTileN;
+    constexpr int kWaves = kWM * kWN;
+    static_assert(kTileM % (8 * kWaves) == 0 && kTileN % (8 * kWaves) == 0, "whole load instructions per wave");
+    constexpr int kLoadsA = kTileM / (8 * kWaves), kLoadsB = kTileN / (8 * kWaves);
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileM * kStepBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kTileN * kStepBytes];
+    __shared__ __attribute__((aligned(16))) float sx_lds[2][kTileM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int r32 = lane & 31, h = lane >> 5;
+    int m0, n0;
+    tile_origin(p, kTileM, kTileN, m0, n0);
+
     const int es = kFp8 ? 1 : 2;
     const int rows_a = p.m - m0 < kTileM ? p.m - m0 : kTileM;
     const int rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
@@ -87,7 +98,6 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
     const __amdgpu_buffer_rsrc_t brs =
         make_buffer(static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(n0) * ldb, rows_b * ldb);
 
-    // Accumulators start at the bias of their column (lane column r32 of each 32x32 block).
     f32x16 acc[kBM][kBN];
 #pragma unroll
     for (int bn = 0; bn < kBN; ++bn) {
@@ -99,75 +109,97 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
             for (int i = 0; i < 16; ++i) acc[bm][bn][i] = b;
     }
 
-    // Thread piece j: row (tid + T j) / 8, 16-byte segment (tid + T j) % 8 of the step's bytes.
-    auto stage_load = [&](GemmStage<S>& st, int step) {
-        const uint32_t kb = static_cast<uint32_t>(step) * kStepBytes;
+    // Loads: wave w fills rows [R w, R w + R) of an operand (R = rows / waves), 8 rows per
+    // instruction; lane l brings the chunk that belongs at position l % 8 of row R w + 8 j + l / 8.
+    uint32_t a_src[kLoadsA], b_src[kLoadsB];
 #pragma unroll
-        for (int j = 0; j < S::kPiecesA; ++j) {
-            const int piece = tid + kThreads * j;
-            const uint32_t row = piece >> 3, seg = piece & 7;
-            st.a[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, row * lda + kb + 16 * seg, 0, 0));
+    for (int j = 0; j < kLoadsA; ++j) {
+        const int row = 8 * kLoadsA * wave + 8 * j + (lane >> 3);
+        a_src[j] = static_cast<uint32_t>(row) * lda + 16u * static_cast<uint32_t>((lane & 7) ^ ((row >> 1) & 7));
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j) {
+        const int row = 8 * kLoadsB * wave + 8 * j + (lane >> 3);
+        b_src[j] = static_cast<uint32_t>(row) * ldb + 16u * static_cast<uint32_t>((lane & 7) ^ ((row >> 1) & 7));
+    }
+    auto dma = [&](int step, int stage) SA_GEMM_INLINE {
+        const uint32_t koff = static_cast<uint32_t>(step) * kStepBytes;
+#pragma unroll
+        for (int j = 0; j < kLoadsA; ++j) {
+            const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                (__attribute__((address_space(3))) void*)&a_lds[stage][(8 * kLoadsA * wave + 8 * j) * kStepBytes]));
+            asm volatile(
+                "s_mov_b32 m0, %0\n\t"
+                "s_nop 0\n\t"
+                "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                :
+                : "s"(dst), "v"(a_src[j] + koff), "s"(ars)
+                : "memory", "m0");
         }
 #pragma unroll
-        for (int j = 0; j < S::kPiecesB; ++j) {
-            const int piece = tid + kThreads * j;
-            const uint32_t row = piece >> 3, seg = piece & 7;
-            st.b[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, row * ldb + kb + 16 * seg, 0, 0));
-        }
-        if constexpr (kFp8) {
-            const int row = m0 + tid;
-            st.sx = tid < kTileM && row < p.m ? p.scale_x[row * p.sx_stride_m + step * p.sx_stride_kb] : 0.0f;
+        for (int j = 0; j < kLoadsB; ++j) {
+            const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                (__attribute__((address_space(3))) void*)&b_lds[stage][(8 * kLoadsB * wave + 8 * j) * kStepBytes]));
+            asm volatile(
+                "s_mov_b32 m0, %0\n\t"
+                "s_nop 0\n\t"
+                "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                :
+                : "s"(dst), "v"(b_src[j] + koff), "s"(brs)
+                : "memory", "m0");
         }
     };
-    auto stage_store = [&](const GemmStage<S>& st, int buf) {
-#pragma unroll
-        for (int j = 0; j < S::kPiecesA; ++j) {
-            const int piece = tid + kThreads * j;
-            *reinterpret_cast<i32x4*>(&a_lds[buf][piece >> 3][16 * (piece & 7)]) = st.a[j];
-        }
-#pragma unroll
-        for (int j = 0; j < S::kPiecesB; ++j) {
-            const int piece = tid + kThreads * j;
-            *reinterpret_cast<i32x4*>(&b_lds[buf][piece >> 3][16 * (piece & 7)]) = st.b[j];
-        }
-        if constexpr (kFp8)
-            if (tid < kTileM) sx_lds[buf][tid] = st.sx;
+    const int steps = p.k / (kStepBytes / es);
+    auto load_sx = [&](int step) SA_GEMM_INLINE {
+        const int row = m0 + tid;
+        return tid < kTileM && row < p.m && step < steps
+                   ? p.scale_x[static_cast<int64_t>(row) * p.sx_stride_m + static_cast<int64_t>(step) * p.sx_stride_kb]
+                   : 0.0f;
     };
-    auto compute = [&](int buf, int step) {
-        const uint8_t* arow[kBM];
-        const uint8_t* brow[kBN];
-#pragma unroll
-        for (int q = 0; q < kBM; ++q) arow[q] = &a_lds[buf][32 * kBM * wm + 32 * q + r32][0];
-#pragma unroll
-        for (int q = 0; q < kBN; ++q) brow[q] = &b_lds[buf][32 * kBN * wn + 32 * q + r32][0];
+
+    // A lane reads rows 32 q + r32 of its wave's blocks; those start on multiples of 32 rows, so
+    // the swizzle of every row it reads is (r32 >> 1) & 7 and the blocks are immediate offsets.
+    const int swz = (r32 >> 1) & 7;
+    const int a_base = (32 * kBM * wm + r32) * kStepBytes;
+    const int b_base = (32 * kBN * wn + r32) * kStepBytes;
+    auto chunk_off = [&](int c) SA_GEMM_INLINE { return 16 * (c ^ swz); };
+    auto compute = [&](int step, auto stage_tag) SA_GEMM_INLINE {
+        constexpr int kStage = decltype(stage_tag)::value;
         if constexpr (!kFp8) {
-            // Four k slices of 16 bf16; lane half h takes k 8h .. 8h + 7 of each slice.
+            // Four k slices of 16 bf16; lane half h takes k 8h .. 8h + 7 of each slice: chunk 2 kk + h.
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
+                const int co = chunk_off(2 * kk + h);
                 bf16x8 av[kBM], bv[kBN];
 #pragma unroll
-                for (int q = 0; q < kBM; ++q) av[q] = *reinterpret_cast<const bf16x8*>(arow[q] + 32 * kk + 16 * h);
+                for (int q = 0; q < kBM; ++q)
+                    av[q] = *reinterpret_cast<const bf16x8*>(&a_lds[kStage][a_base + 32 * q * kStepBytes + co]);
 #pragma unroll
-                for (int q = 0; q < kBN; ++q) bv[q] = *reinterpret_cast<const bf16x8*>(brow[q] + 32 * kk + 16 * h);
+                for (int q = 0; q < kBN; ++q)
+                    bv[q] = *reinterpret_cast<const bf16x8*>(&b_lds[kStage][b_base + 32 * q * kStepBytes + co]);
 #pragma unroll
                 for (int bm = 0; bm < kBM; ++bm)
 #pragma unroll
                     for (int bn = 0; bn < kBN; ++bn) acc[bm][bn] = mfma32x32x16(av[bm], bv[bn], acc[bm][bn]);
             }
         } else {
-            // Two k slices of 64 FP8; lane half h takes bytes 32h .. 32h + 31 of each slice (the
+            // Two k slices of 64 FP8; lane half h takes chunks 4 sl + 2 h and 4 sl + 2 h + 1 (the
             // same bytes for A and B, so the product pairs equal k whatever order the unit uses).
-            // Each block's two products go into a temporary that is promoted at once:
             // acc += part * scale_x[row] * scale_w (the wave's columns share one weight scale).
             const int nb = (n0 + 32 * kBN * wn) / 128;
-            const float sw = p.scale_w[static_cast<int64_t>(nb) * p.sw_stride_nb + step * p.sw_stride_kb];
+            const float sw = p.scale_w[static_cast<int64_t>(nb) * p.sw_stride_nb + static_cast<int64_t>(step) * p.sw_stride_kb];
+            int co[2][2];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) co[sl][e] = chunk_off(4 * sl + 2 * h + e);
             i32x8 bv[2][kBN];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int q = 0; q < kBN; ++q) {
-                    const i32x4 b0 = *reinterpret_cast<const i32x4*>(brow[q] + 64 * sl + 32 * h);
-                    const i32x4 b1 = *reinterpret_cast<const i32x4*>(brow[q] + 64 * sl + 32 * h + 16);
+                    const i32x4 b0 = *reinterpret_cast<const i32x4*>(&b_lds[kStage][b_base + 32 * q * kStepBytes + co[sl][0]]);
+                    const i32x4 b1 = *reinterpret_cast<const i32x4*>(&b_lds[kStage][b_base + 32 * q * kStepBytes + co[sl][1]]);
                     bv[sl][q] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
 #pragma unroll
@@ -175,15 +207,15 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
                 i32x8 av[2];
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl) {
-                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow[bm] + 64 * sl + 32 * h);
-                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow[bm] + 64 * sl + 32 * h + 16);
+                    const i32x4 a0 = *reinterpret_cast<const i32x4*>(&a_lds[kStage][a_base + 32 * bm * kStepBytes + co[sl][0]]);
+                    const i32x4 a1 = *reinterpret_cast<const i32x4*>(&a_lds[kStage][a_base + 32 * bm * kStepBytes + co[sl][1]]);
                     av[sl] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
                 float c[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const f32x4 sx4 =
-                        *reinterpret_cast<const f32x4*>(&sx_lds[buf][32 * kBM * wm + 32 * bm + 8 * g + 4 * h]);
+                        *reinterpret_cast<const f32x4*>(&sx_lds[kStage][32 * kBM * wm + 32 * bm + 8 * g + 4 * h]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) c[4 * g + e] = sx4[e] * sw;
                 }
@@ -198,47 +230,33 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
             }
         }
     };
-
-    // bf16 with four waves: two steps of loads in flight; FP8 and the eight-wave tiles (no registers
-    // to spare): one. Step i + 1 goes from registers into the other buffer after step i is
-    // multiplied; one barrier per step.
-    const int steps = p.k / (kStepBytes / es);
-    GemmStage<S> ra, rb;
-    if constexpr (kFp8 || kWM * kWN > 4) {
-        stage_load(ra, 0);
-        stage_store(ra, 0);
+    // Step i (stage i % 2): products of step i while the loads of step i + 1 land; the wave waits
+    // for its own loads (and, FP8, stores the next step's row scales), and one barrier publishes
+    // step i + 1 and frees stage i % 2 for the loads of step i + 2. Loads past K read bytes of the
+    // slices' following rows (or zeros past their end) into a stage no step reads.
+    auto step_body = [&](int i, auto stage_tag) SA_GEMM_INLINE {
+        constexpr int kStage = decltype(stage_tag)::value;
+        float sx_next = 0.0f;
+        if constexpr (kFp8) sx_next = load_sx(i + 1);
+        compute(i, stage_tag);
+        if constexpr (kFp8)
+            if (tid < kTileM) sx_lds[kStage ^ 1][tid] = sx_next;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        for (int i = 0; i < steps; ++i) {
-            if (i + 1 < steps) stage_load(ra, i + 1);
-            // bf16: a wave issuing its MFMAs goes ahead of its SIMD partner's LDS stores (measured
-            // 2-3% faster at 4096^3 and 8192 x 8192 x 4096; FP8 measured slower with it).
-            if constexpr (!kFp8) __builtin_amdgcn_s_setprio(1);
-            compute(i & 1, i);
-            if constexpr (!kFp8) __builtin_amdgcn_s_setprio(0);
-            if (i + 1 < steps) stage_store(ra, (i + 1) & 1);
-            __syncthreads();
-        }
-    } else {
-        // Unconditional prefetch two steps ahead: loads past the K extent stay inside the rows'
-        // buffer range (or read zeros) and are never stored, and with no branch around them the
-        // compiler waits for just the older step's loads before each LDS store.
-        stage_load(ra, 0);
-        stage_store(ra, 0);
-        stage_load(ra, 1);
-        __syncthreads();
-        for (int i = 0; i < steps;) {
-            stage_load(rb, i + 2);
-            compute(i & 1, i);
-            stage_store(ra, (i + 1) & 1);
-            __syncthreads();
-            if (++i >= steps) break;
-            stage_load(ra, i + 2);
-            compute(i & 1, i);
-            stage_store(rb, (i + 1) & 1);
-            __syncthreads();
-            ++i;
-        }
+        dma(i + 2, kStage);
+    };
+    if constexpr (kFp8)
+        if (tid < kTileM) sx_lds[0][tid] = load_sx(0);
+    dma(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    dma(1, 1);
+    for (int i = 0; i < steps; i += 2) {
+        step_body(i, std::integral_constant<int, 0>());
+        if (i + 1 < steps) step_body(i + 1, std::integral_constant<int, 1>());
     }
+    // Loads still in flight target LDS that must not be released under them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     // Epilogue: lane column r32 of each block, rows 8 (i / 4) + 4 h + (i % 4).
 #pragma unroll
@@ -261,23 +279,25 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
 }
 
 template <bool kFp8, int kBM, int kBN, int kWM, int kWN>
-hipError_t launch_shape(const GemmParams& p, hipStream_t stream) {
+hipError_t launch_dma_shape(const GemmParams& p, hipStream_t stream) {
     using S = GemmShape<kBM, kBN, kWM, kWN>;
     const int64_t tiles = static_cast<int64_t>((p.m + S::kTileM - 1) / S::kTileM) * ((p.n + S::kTileN - 1) / S::kTileN);
-    gemm_bias_kernel<kFp8, kBM, kBN, kWM, kWN>
+    gemm_bias_dma_kernel<kFp8, kBM, kBN, kWM, kWN>
         <<<dim3(static_cast<unsigned>(tiles)), dim3(S::kThreads), 0, stream>>>(p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// FP8: 128 x 128 tiles, four waves of 2 x 2 blocks (two work-groups per CU). bf16: 256 x 256 tiles,
-// eight waves of 4 x 2 blocks, where the problem has rows and columns for them (fewer operand
-// reads and LDS writes per flop); 128 x 128 otherwise.
+// FP8: 128 x 128 tiles (the 256 x 256 form needs more than the 256 registers a wave has at two
+// waves per SIMD). bf16: 256 x 256 tiles when there are at least 128 of them (fewer operand reads
+// per flop), else 128 x 128 (more work-groups for small problems: 300 x 640 x 512 took 9.9 us
+// against 20.8 us on 256 x 256 tiles).
 hipError_t launch_gemm_bias(const GemmParams& p, bool fp8, hipStream_t stream) {
-    if (fp8) return launch_shape<true, 2, 2, 2, 2>(p, stream);
-    if (p.m >= 256 && p.n >= 256) return launch_shape<false, 4, 2, 2, 4>(p, stream);
-    return launch_shape<false, 2, 2, 2, 2>(p, stream);
+    if (fp8) return launch_dma_shape<true, 2, 2, 2, 2>(p, stream);
+    const int64_t tiles256 = static_cast<int64_t>((p.m + 255) / 256) * ((p.n + 255) / 256);
+    if (tiles256 >= 128) return launch_dma_shape<false, 4, 2, 2, 4>(p, stream);
+    return launch_dma_shape<false, 2, 2, 2, 2>(p, stream);
 }
 
 }  // namespace sinkattn

@@ -67,27 +67,68 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr float kZeroRefLimit = 16.0f;
 constexpr float kFastSumLimit = 18446744073709551616.0f;  // 2^64
 
-// Maps a linear query-tile index to (sequence, first position). Tiles are numbered sequence by
-// sequence; within a sequence index 0 is the tile holding the last positions. Returns false for
-// the padding tiles past the last one.
-__device__ bool locate_tile(const int32_t* cu_q, int num_seqs, int total_q, int positions_per_tile,
-                            int tile, int& seq, int& first_pos, int& q_start, int& q_len) {
-    int before = 0;
-    for (int s = 0; s < num_seqs; ++s) {
-        // Clamped so that malformed prefix sums cannot move a row outside [0, total_q).
-        const int start = min(max(cu_q[s], 0), total_q);
-        const int len = min(max(cu_q[s + 1] - start, 0), total_q - start);
-        const int tiles = (len + positions_per_tile - 1) / positions_per_tile;
-        if (tile < before + tiles) {
-            seq = s;
-            first_pos = (tiles - 1 - (tile - before)) * positions_per_tile;
-            q_start = start;
-            q_len = len;
-            return true;
+// Maps a linear query-tile index to its sequence and first position. Sequence s owns tile indices
+// [V(s), V(s + 1)) with V(s) = floor(start(s) / P) + s (P positions per tile): V(s + 1) - V(s) =
+// floor(end / P) - floor(start / P) + 1 >= ceil(len / P), so each sequence has room for its tiles
+// plus at most one padding index, V(B) <= ceil(Tq / P) + B bounds the grid, and V(s) needs only
+// start(s), so the search is parallel: each step the 64 lanes test 64 evenly spaced sequences with
+// one load each and keep the last one whose V is at most the tile index (V grows with s). Within a
+// sequence index 0 is the tile holding the last positions. The lanes of the last step also read
+// the sequence's key bounds, so every prefix sum the work-group needs arrives in one round trip.
+// Returns false for padding indices. Starts and lengths are clamped to [0, total) so that broken
+// prefix sums cannot move a row out of bounds (the tiles then computed are unspecified).
+struct TileSpan {
+    int seq, first_pos, q_start, q_len, k_start, k_len;
+};
+
+__device__ bool locate_tile(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int total_q, int total_k,
+                            int positions_per_tile, int tile, int lane, TileSpan& t) {
+    auto clamp_start = [](int x, int total) { return min(max(x, 0), total); };
+    int lo = 0, n = num_seqs;
+    // This lane's probe of the last step: prefix sums at s and s + 1 (raw, clamped below).
+    int q0 = 0, q1 = 0, k0 = 0, k1 = 0;
+    int last = 0;  // lane whose probe is the sequence found
+    bool probed = false;
+    while (n > 1) {
+        const int step = (n + 63) >> 6;
+        const int s = lo + lane * step;
+        bool ok = false;
+        if (s < lo + n) {
+            q0 = cu_q[s];
+            q1 = cu_q[s + 1];
+            k0 = cu_k[s];
+            k1 = cu_k[s + 1];
+            ok = clamp_start(q0, total_q) / positions_per_tile + s <= tile;
         }
-        before += tiles;
+        // Lane 0 tests lo, whose V is at most the tile index for well-formed prefix sums.
+        const int k = max(__popcll(__ballot(ok)), 1);
+        lo += (k - 1) * step;
+        n = min(step, n - (k - 1) * step);
+        last = k - 1;
+        probed = true;
     }
-    return false;
+    int sq0, sq1, sk0, sk1;
+    if (probed) {
+        sq0 = __builtin_amdgcn_readlane(q0, last);
+        sq1 = __builtin_amdgcn_readlane(q1, last);
+        sk0 = __builtin_amdgcn_readlane(k0, last);
+        sk1 = __builtin_amdgcn_readlane(k1, last);
+    } else {
+        sq0 = cu_q[0];
+        sq1 = cu_q[1];
+        sk0 = cu_k[0];
+        sk1 = cu_k[1];
+    }
+    t.seq = lo;
+    t.q_start = clamp_start(sq0, total_q);
+    t.q_len = min(max(sq1 - t.q_start, 0), total_q - t.q_start);
+    t.k_start = clamp_start(sk0, total_k);
+    t.k_len = min(max(sk1 - t.k_start, 0), total_k - t.k_start);
+    const int tiles = (t.q_len + positions_per_tile - 1) / positions_per_tile;
+    const int local = tile - (t.q_start / positions_per_tile + lo);
+    if (local < 0 || local >= tiles) return false;
+    t.first_pos = (tiles - 1 - local) * positions_per_tile;
+    return true;
 }
 
 template <bool kSplit>
@@ -114,13 +155,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     const int group = p.num_q_heads / p.num_kv_heads;
     const int positions_per_tile = kRowsPerTile / group;
 
-    int seq, first_pos, q_start, q_len;
-    if (!locate_tile(p.cu_seqlens_q, p.num_seqs, static_cast<int>(p.total_q), positions_per_tile, tile,
-                     seq, first_pos, q_start, q_len))
+    TileSpan span;
+    if (!locate_tile(p.cu_seqlens_q, p.cu_seqlens_k, p.num_seqs, static_cast<int>(p.total_q),
+                     static_cast<int>(p.total_k), positions_per_tile, tile, lane, span))
         return;
-    const int total_k = static_cast<int>(p.total_k);
-    const int k_start = min(max(p.cu_seqlens_k[seq], 0), total_k);
-    const int k_len = min(max(p.cu_seqlens_k[seq + 1] - k_start, 0), total_k - k_start);
+    const int first_pos = span.first_pos, q_start = span.q_start, q_len = span.q_len;
+    const int k_start = span.k_start, k_len = span.k_len;
     const int offset = k_len - q_len;  // bottom-right causal alignment
 
     // Rows of this lane: column block cb -> tile row 64 wave + 32 cb + col. S^T comes out of the

@@ -156,6 +156,9 @@ PREFILL_SMALL = [
     ("mha_long", [700], None, 4, 4, True, (-2, 2)),
     ("group128", [20, 3], None, 128, 1, True, (-2, 2)),
     ("append_long", [100], [2000], 64, 8, True, (-2, 2)),
+    # More sequences than a wave has lanes: the tile search takes two and three 64-way steps.
+    ("many_seqs_100", [(i * 37) % 71 for i in range(100)], None, 64, 8, True, (-2, 2)),
+    ("many_seqs_4500", [(i * 7) % 5 for i in range(4500)], None, 16, 8, True, (-2, 2)),
 ]
 
 
@@ -196,6 +199,7 @@ PREFILL_SPLIT_CASES = [
     ("more_splits_than_tiles", [70], [300], 64, 8, True, 40),
     ("one_split", [200], None, 64, 8, True, 1),
     ("group16_append", [33, 5], [700, 64], 64, 4, True, 6),
+    ("many_seqs", [(i * 13) % 40 for i in range(130)], [(i * 13) % 40 + 50 for i in range(130)], 64, 8, True, 3),
 ]
 
 

@@ -4,18 +4,19 @@
 // Source: "GPT-OSS on Day 0" (Perplexity). Section "GPT-OSS on Hopper" picks FP8 with 128x128 block
 // scaling and a bias term for the GEMM kernels; section "Kernels for GPT-OSS" adds the bias by
 // starting the accumulator registers at bias values loaded from memory once per output block. Here
-// every 32x32 accumulator block starts at the bias: a lane's 16 accumulators share one output
-// column (the MFMA C layout), so the bias costs one load per lane and block and no epilogue pass.
+// every 32x32 accumulator block starts at the bias of its columns, loaded once per lane.
 //
 // Work-groups: 256 x 256 output tiles of eight waves of 128 x 64 (4 x 2 blocks, two waves per SIMD)
-// for bf16 problems large enough to fill the chip with them, else 128 x 128 tiles of four waves of
-// 64 x 64 (2 x 2 blocks, two work-groups per CU); FP8 always the latter. Blocks are
-// v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales for FP8.
-// Each K step's 128 bytes of every X and W row (64 bf16 or 128 FP8 values = one scale block) go
-// from memory straight into LDS with buffer_load ... lds, into two unpadded, swizzled stages; the
-// next step's loads are in flight while the current one is multiplied. FP8: each 128-wide k block
-// is multiplied into a temporary accumulator, then added to the running one times
-// scale_x[row, kb] * scale_w[column block, kb] (rows' scales staged in LDS beside each stage).
+// for problems large enough to fill the chip with them, else 128 x 128 tiles of four waves of
+// 64 x 64 (2 x 2 blocks, two work-groups per CU). Blocks are v_mfma_f32_32x32x16_bf16, or
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales for FP8, with W rows as the A operand and
+// X rows as the B operand: a block holds Y^T, so a lane owns one output row and four runs of four
+// consecutive columns. Each K step's 128 bytes of every X and W row (64 bf16 or 128 FP8 values = one
+// scale block) go from memory straight into LDS with buffer_load ... lds, into two unpadded,
+// swizzled stages; the next step's loads are in flight while the current one is multiplied. FP8:
+// each 128-wide k block is multiplied into a temporary accumulator, then added to the running one
+// times scale_x[row, kb] * scale_w[column block, kb], one factor per lane and block row (rows'
+// scales staged in LDS beside each stage). bf16 output leaves through LDS as 16-byte row stores.
 // Tiles are spread XCD-aware: each XCD takes a contiguous range of tile indices, walked in groups of
 // 8 tile-rows so the X and W panels a group shares stay in that XCD's L2.
 
@@ -77,8 +78,16 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
     constexpr int kWaves = kWM * kWN;
     static_assert(kTileM % (8 * kWaves) == 0 && kTileN % (8 * kWaves) == 0, "whole load instructions per wave");
     constexpr int kLoadsA = kTileM / (8 * kWaves), kLoadsB = kTileN / (8 * kWaves);
-    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileM * kStepBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kTileN * kStepBytes];
+    // One LDS area: the two operand stages during the K loop, then (bf16 output) each wave's
+    // output block on its way to 16-byte row stores.
+    constexpr int kABytes = kTileM * kStepBytes, kBBytes = kTileN * kStepBytes;
+    constexpr int kOutRowBytes = 32 * kBN * 2;                     // one row of a wave's bf16 block
+    constexpr int kWaveOutBytes = 32 * kBM * kOutRowBytes;
+    static_assert(kOutRowBytes == 128, "eight 16-byte chunks per output row");
+    static_assert(kWaves * kWaveOutBytes <= 2 * (kABytes + kBBytes), "output blocks fit in the operand stages");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kABytes + kBBytes)];
+    auto a_lds = reinterpret_cast<uint8_t (*)[kABytes]>(smem);
+    auto b_lds = reinterpret_cast<uint8_t (*)[kBBytes]>(smem + 2 * kABytes);
     __shared__ __attribute__((aligned(16))) float sx_lds[2][kTileM];
 
     const int tid = threadIdx.x;
@@ -98,16 +107,18 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
     const __amdgpu_buffer_rsrc_t brs =
         make_buffer(static_cast<const uint8_t*>(p.w) + static_cast<int64_t>(n0) * ldb, rows_b * ldb);
 
+    // Block (bm, bn) holds Y^T: W rows (n) are the MFMA's A operand and X rows (m) its B operand,
+    // so lane column r32 is one output row m and register i is column 8 (i / 4) + 4 h + (i % 4).
     f32x16 acc[kBM][kBN];
 #pragma unroll
-    for (int bn = 0; bn < kBN; ++bn) {
-        const int n = n0 + 32 * kBN * wn + 32 * bn + r32;
-        const float b = p.bias != nullptr && n < p.n ? p.bias[n] : 0.0f;
+    for (int bn = 0; bn < kBN; ++bn)
 #pragma unroll
-        for (int bm = 0; bm < kBM; ++bm)
+        for (int i = 0; i < 16; ++i) {
+            const int n = n0 + 32 * kBN * wn + 32 * bn + 8 * (i / 4) + 4 * h + (i % 4);
+            const float b = p.bias != nullptr && n < p.n ? p.bias[n] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[bm][bn][i] = b;
-    }
+            for (int bm = 0; bm < kBM; ++bm) acc[bm][bn][i] = b;
+        }
 
     // Loads: wave w fills rows [R w, R w + R) of an operand (R = rows / waves), 8 rows per
     // instruction; lane l brings the chunk that belongs at position l % 8 of row R w + 8 j + l / 8.
@@ -180,7 +191,7 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
 #pragma unroll
                 for (int bm = 0; bm < kBM; ++bm)
 #pragma unroll
-                    for (int bn = 0; bn < kBN; ++bn) acc[bm][bn] = mfma32x32x16(av[bm], bv[bn], acc[bm][bn]);
+                    for (int bn = 0; bn < kBN; ++bn) acc[bm][bn] = mfma32x32x16(bv[bn], av[bm], acc[bm][bn]);
             }
         } else {
             // Two k slices of 64 FP8; lane half h takes chunks 4 sl + 2 h and 4 sl + 2 h + 1 (the
@@ -202,30 +213,40 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
                     const i32x4 b1 = *reinterpret_cast<const i32x4*>(&b_lds[kStage][b_base + 32 * q * kStepBytes + co[sl][1]]);
                     bv[sl][q] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
-#pragma unroll
-            for (int bm = 0; bm < kBM; ++bm) {
-                i32x8 av[2];
+            auto load_a = [&](int bm, i32x8 (&av)[2]) SA_GEMM_INLINE {
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl) {
                     const i32x4 a0 = *reinterpret_cast<const i32x4*>(&a_lds[kStage][a_base + 32 * bm * kStepBytes + co[sl][0]]);
                     const i32x4 a1 = *reinterpret_cast<const i32x4*>(&a_lds[kStage][a_base + 32 * bm * kStepBytes + co[sl][1]]);
                     av[sl] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
-                float c[16];
+            };
+            // One block-row at a time, the next row's operands read while this one is multiplied:
+            // the accumulators of a row are pinned before the reads of the row after next, which
+            // keeps the compiler from reading every row's operands up front (more registers than
+            // the 256-column tile has).
+            i32x8 av[2], av_next[2];
+            load_a(0, av);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 sx4 =
-                        *reinterpret_cast<const f32x4*>(&sx_lds[kStage][32 * kBM * wm + 32 * bm + 8 * g + 4 * h]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) c[4 * g + e] = sx4[e] * sw;
-                }
+            for (int bm = 0; bm < kBM; ++bm) {
+                if (bm + 1 < kBM) load_a(bm + 1, av_next);
+                // The lane's output row is m = r32 of block bm: one scale for all its registers.
+                const float c = sx_lds[kStage][32 * kBM * wm + 32 * bm + r32] * sw;
 #pragma unroll
                 for (int bn = 0; bn < kBN; ++bn) {
-                    f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[0], bv[0][bn], zero_f32x16(),
+                    f32x16 part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[0][bn], av[0], zero_f32x16(),
                                                                                    0, 0, 0, 127, 0, 127);
-                    part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[1], bv[1][bn], part, 0, 0, 0, 127, 0, 127);
+                    part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[1][bn], av[1], part, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[bm][bn][i] = fmaf(part[i], c[i], acc[bm][bn][i]);
+                    for (int i = 0; i < 16; ++i) acc[bm][bn][i] = fmaf(part[i], c, acc[bm][bn][i]);
+                }
+                if constexpr (kBM > 2) {
+#pragma unroll
+                    for (int bn = 0; bn < kBN; ++bn) asm volatile("" : "+v"(acc[bm][bn]) : : "memory");
+                }
+                if (bm + 1 < kBM) {
+                    av[0] = av_next[0];
+                    av[1] = av_next[1];
                 }
             }
         }
@@ -258,24 +279,82 @@ __global__ __launch_bounds__(64 * kWM * kWN, kWM * kWN == 4 ? 2 : 1) void gemm_b
     // Loads still in flight target LDS that must not be released under them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // Epilogue: lane column r32 of each block, rows 8 (i / 4) + 4 h + (i % 4).
+    // Epilogue: lane column r32 of each block is output row m; registers 4 g .. 4 g + 3 are the
+    // consecutive columns 8 g + 4 h .. + 3. bf16 output with 16-byte aligned rows goes through LDS:
+    // each wave writes its block row-major (16-byte chunk c of row r at c ^ (r & 7): the 8-byte
+    // writes of 32 rows and the 16-byte reads of 8 rows hit distinct banks), then stores whole
+    // 128-byte row pieces, 16 bytes a lane. Otherwise every lane stores its four columns itself.
+    const int es_y = p.y_is_bf16 ? 2 : 4;
+    const uintptr_t y_addr = reinterpret_cast<uintptr_t>(p.y);
+    const int m_wave = m0 + 32 * kBM * wm, n_wave = n0 + 32 * kBN * wn;
+    if (p.y_is_bf16 && y_addr % 16 == 0 && (p.ldy * 2) % 16 == 0) {
+        __syncthreads();  // every wave has read its last operands (no loads are in flight)
+        uint8_t* ow = smem + wave * kWaveOutBytes;
 #pragma unroll
-    for (int bm = 0; bm < kBM; ++bm)
+        for (int bm = 0; bm < kBM; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < kBN; ++bn) {
-            const int n = n0 + 32 * kBN * wn + 32 * bn + r32;
-            if (n >= p.n) continue;
+            for (int bn = 0; bn < kBN; ++bn)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + 32 * kBM * wm + 32 * bm + 8 * (i / 4) + 4 * h + (i % 4);
-                if (m >= p.m) continue;
-                const int64_t off = static_cast<int64_t>(m) * p.ldy + n;
-                if (p.y_is_bf16)
-                    static_cast<__bf16*>(p.y)[off] = static_cast<__bf16>(acc[bm][bn][i]);
-                else
-                    static_cast<float*>(p.y)[off] = acc[bm][bn][i];
+                for (int g = 0; g < 4; ++g) {
+                    const int row = 32 * bm + r32;
+                    const int chunk = 4 * bn + g;
+                    bf16x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(acc[bm][bn][4 * g + e]);
+                    *reinterpret_cast<bf16x4*>(ow + row * kOutRowBytes + 16 * (chunk ^ (row & 7)) + 8 * h) = o;
+                }
+#pragma unroll
+        for (int j = 0; j < kWaveOutBytes / 1024; ++j) {
+            const int row = 8 * j + (lane >> 3), chunk = lane & 7;
+            const bf16x8 o = *reinterpret_cast<const bf16x8*>(ow + row * kOutRowBytes + 16 * (chunk ^ (row & 7)));
+            const int m = m_wave + row, n = n_wave + 8 * chunk;
+            if (m >= p.m) continue;
+            __bf16* dst = static_cast<__bf16*>(p.y) + static_cast<int64_t>(m) * p.ldy + n;
+            if (n + 7 < p.n) {
+                *reinterpret_cast<bf16x8*>(dst) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < p.n) dst[e] = o[e];
             }
         }
+        return;
+    }
+    const bool vec_ok = y_addr % (4 * es_y) == 0 && (p.ldy * es_y) % (4 * es_y) == 0;
+#pragma unroll
+    for (int bm = 0; bm < kBM; ++bm) {
+        const int m = m_wave + 32 * bm + r32;
+        if (m >= p.m) continue;
+#pragma unroll
+        for (int bn = 0; bn < kBN; ++bn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n_wave + 32 * bn + 8 * g + 4 * h;
+                const int64_t off = static_cast<int64_t>(m) * p.ldy + n;
+                if (vec_ok && n + 3 < p.n) {
+                    if (p.y_is_bf16) {
+                        bf16x4 o;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(acc[bm][bn][4 * g + e]);
+                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.y) + off) = o;
+                    } else {
+                        f32x4 o;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = acc[bm][bn][4 * g + e];
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(p.y) + off) = o;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (n + e >= p.n) continue;
+                        if (p.y_is_bf16)
+                            static_cast<__bf16*>(p.y)[off + e] = static_cast<__bf16>(acc[bm][bn][4 * g + e]);
+                        else
+                            static_cast<float*>(p.y)[off + e] = acc[bm][bn][4 * g + e];
+                    }
+                }
+            }
+    }
 }
 
 template <bool kFp8, int kBM, int kBN, int kWM, int kWN>
@@ -289,13 +368,15 @@ hipError_t launch_dma_shape(const GemmParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// FP8: 128 x 128 tiles (the 256 x 256 form needs more than the 256 registers a wave has at two
-// waves per SIMD). bf16: 256 x 256 tiles when there are at least 128 of them (fewer operand reads
-// per flop), else 128 x 128 (more work-groups for small problems: 300 x 640 x 512 took 9.9 us
-// against 20.8 us on 256 x 256 tiles).
+// 256 x 256 tiles when there are at least 128 of them (fewer operand reads per flop), else 128 x 128
+// (more work-groups for small problems: bf16 300 x 640 x 512 took 9.9 us against 20.8 us on
+// 256 x 256 tiles).
 hipError_t launch_gemm_bias(const GemmParams& p, bool fp8, hipStream_t stream) {
-    if (fp8) return launch_dma_shape<true, 2, 2, 2, 2>(p, stream);
     const int64_t tiles256 = static_cast<int64_t>((p.m + 255) / 256) * ((p.n + 255) / 256);
+    if (fp8) {
+        if (tiles256 >= 128) return launch_dma_shape<true, 4, 2, 2, 4>(p, stream);
+        return launch_dma_shape<true, 2, 2, 2, 2>(p, stream);
+    }
     if (tiles256 >= 128) return launch_dma_shape<false, 4, 2, 2, 4>(p, stream);
     return launch_dma_shape<false, 2, 2, 2, 2>(p, stream);
 }

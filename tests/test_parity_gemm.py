@@ -59,9 +59,8 @@ BF16_CASES = [
     ("one_column", 129, 1, 128, True, torch.bfloat16),
     ("no_bias_f32_out", 200, 260, 320, False, torch.float32),
     ("deep_k_4096", 128, 256, 4096, True, torch.bfloat16),
-    # M, N >= 256 take the 256 x 256 tiles of eight waves; ragged in both
-    ("big_tiles_ragged_300x520x256", 300, 520, 256, True, torch.bfloat16),
-    ("big_tiles_f32_out_512x256x128", 512, 256, 128, True, torch.float32),
+    ("ragged_300x520x256", 300, 520, 256, True, torch.bfloat16),
+    ("f32_out_512x256x128", 512, 256, 128, True, torch.float32),
 ]
 
 
@@ -164,3 +163,42 @@ def test_linear_full_size_4096_sampled_rows(fp8):
         ref, s_abs = oracle.gemm_bias(xd, wd, b.double().numpy()), np.abs(xd) @ np.abs(wd).T
     _check(y[torch.from_numpy(rows).cuda()], ref, s_abs, k, f"{'fp8' if fp8 else 'bf16'} 4096^3 sampled",
            u_acc=FP8_U_ACC if fp8 else 2.0 ** -24)
+
+
+# Problems with at least 128 tiles of 256 x 256 take the eight-wave 256 x 256 tiles (bf16 and FP8).
+# Output forms: bf16 rows 16-byte aligned go through LDS to 16-byte row stores, here with a last
+# chunk only partly inside N (a view of a wider buffer); a misaligned bf16 base and fp32 output
+# take the per-lane stores.
+FULL_CHIP_OUTPUTS = ["bf16_lds_partial_chunk", "bf16_misaligned", "f32"]
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("out_kind", FULL_CHIP_OUTPUTS)
+def test_linear_full_chip_tiles_ragged(fp8, out_kind):
+    sa = _sa()
+    m, n, k = 2900, 2997, 256
+    if out_kind == "f32":
+        y_buf = torch.zeros((m, n), dtype=torch.float32, device="cuda")
+        y = y_buf
+    else:
+        y_buf = torch.zeros((m, 3008), dtype=torch.bfloat16, device="cuda")
+        y = y_buf[:, :n] if out_kind == "bf16_lds_partial_chunk" else y_buf[:, 1:n + 1]
+    if fp8:
+        x, sx, w, sw, b = _fp8_case(m, n, k, 51)
+        sa.linear_fp8_block_scaled(x.cuda(), sx.cuda(), w.cuda(), sw.cuda(), b.cuda(), out=y)
+        torch.cuda.synchronize()
+        ref, s_abs = _fp8_ref(x, sx, w, sw, b)
+    else:
+        x, w = _bf16((m, k), 52), _bf16((n, k), 53)
+        b = torch.randn(n, generator=torch.Generator().manual_seed(54))
+        sa.linear_bias(x.cuda(), w.cuda(), b.cuda(), out=y)
+        torch.cuda.synchronize()
+        xd, wd = x.double().numpy(), w.double().numpy()
+        ref, s_abs = oracle.gemm_bias(xd, wd, b.double().numpy()), np.abs(xd) @ np.abs(wd).T
+    _check(y, ref, s_abs, k, f"{'fp8' if fp8 else 'bf16'} 2900x2997x256 {out_kind}",
+           u_acc=FP8_U_ACC if fp8 else 2.0 ** -24)
+    if out_kind != "f32":
+        # Nothing written outside the view.
+        lo, hi = (0, n) if out_kind == "bf16_lds_partial_chunk" else (1, n + 1)
+        assert torch.all(y_buf[:, :lo] == 0) and torch.all(y_buf[:, hi:] == 0)
+

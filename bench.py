@@ -116,6 +116,43 @@ def _time_graph(graph, calls, torch, replays=20):
     return per_call[mid] if replays % 2 else 0.5 * (per_call[mid - 1] + per_call[mid])
 
 
+# Instructions per wave and iteration of each sinkattn_ceiling_issue kind (include/sinkattn_ceilings.h).
+ISSUE_KINDS = {"v_exp_f32": (0, 16), "v_mul_f32": (1, 16), "v_cvt_pk_bf16_f32": (2, 16), "v_fma_f32": (3, 16),
+               "mfma_32x32x16_bf16": (4, 4), "mfma_16x16x32_bf16": (5, 4), "mfma32_plus_4_exp": (6, 4),
+               "prefill_tile_mix_per_tile": (7, 0.25)}
+
+
+def measure_issue_cycles(lib, torch, dev, sink, blocks=512, iters=20000):
+    """SIMD cycles per instruction of the prefill's inner-loop instructions, two waves per SIMD (512
+    work-groups of four waves on 256 CUs): kernel time x the clock the loop ran at (shader cycles
+    over 100 MHz ticks, recorded in the kernel) / instructions per SIMD. 'mfma32_plus_4_exp' is per
+    MFMA with its four exponentials; 'prefill_tile_mix_per_tile' is per 64 x 64 tile and wave (32 + 8
+    MFMAs, 64 mul -> exp, 32 packs) with nothing else to wait for."""
+    import ctypes
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    out = {}
+    for name, (kind, per_iter) in ISSUE_KINDS.items():
+        def launch(i, k=kind):
+            rc = lib.sinkattn_ceiling_issue(k, blocks, iters, ctypes.c_void_p(clk.data_ptr()),
+                                            ctypes.c_void_p(sink.data_ptr()),
+                                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"issue-cost launch failed ({rc})")
+        launch(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch(0)
+        e1.record()
+        torch.cuda.synchronize()
+        t = clk.view(blocks, 2).double()
+        ghz = float(t[:, 0].sum() / (t[:, 1].sum() / 100e6)) / 1e9
+        waves_per_simd = blocks / 256
+        cycles = e0.elapsed_time(e1) * 1e-3 * ghz * 1e9 / (iters * waves_per_simd)
+        out[name] = round(cycles / per_iter, 2)
+    return out
+
+
 def measure_ceilings(torch, dev):
     """Measured ceilings (libsinkattn_ceilings, include/sinkattn_ceilings.h): the HBM streaming-read
     rate of a plain kernel, over 2 GiB and over decode-sized 128 MiB reads rotating through that
@@ -129,6 +166,8 @@ def measure_ceilings(torch, dev):
     lib.sinkattn_ceiling_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.sinkattn_ceiling_mfma_bf16_flop.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.sinkattn_ceiling_mfma_bf16_flop.restype = ctypes.c_double
+    lib.sinkattn_ceiling_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
     sink = torch.zeros(4, dtype=torch.uint8, device=dev)
     big = 2 * 2**30
     buf = torch.empty(big, dtype=torch.uint8, device=dev).fill_(1)
@@ -170,6 +209,7 @@ def measure_ceilings(torch, dev):
         best = max(best, (lib.sinkattn_ceiling_mfma_bf16_flop(blocks, 4000) / (ms * 1e-3) / 1e12, blocks))
     res["mfma_bf16_loop_tflops"] = round(best[0], 1)
     res["mfma_bf16_loop_blocks"] = best[1]
+    res["issue_cycles"] = measure_issue_cycles(lib, torch, dev, sink)
     n = 8192
     gen = torch.Generator().manual_seed(1010)
     a = torch.randn((n, n), generator=gen).to(torch.bfloat16).to(dev)

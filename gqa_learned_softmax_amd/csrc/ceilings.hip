@@ -1,8 +1,9 @@
 // Measured ceilings of the MI355X that runs the library: the rate at which a plain kernel streams
-// bytes out of HBM, and the rate at which the matrix cores retire bf16 MFMAs at the clock the chip
-// holds under that load. They are the denominators the benchmark reports beside the published peaks
-// (8 TB/s HBM, 2.5 PFLOP/s dense bf16). Measurement only: nothing in libsinkattn calls them, and they
-// are built into a library of their own (libsinkattn_ceilings.so).
+// bytes out of HBM, the rate at which the matrix cores retire bf16 MFMAs at the clock the chip
+// holds under that load, and what the instructions of the prefill's inner loop cost a SIMD. They
+// are the denominators the benchmark reports beside the published peaks (8 TB/s HBM, 2.5 PFLOP/s
+// dense bf16). Measurement only: nothing in libsinkattn calls them, and they are built into a
+// library of their own (libsinkattn_ceilings.so).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,6 +59,92 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* out) {
     if (s == -1.0f) out[0] = s;  // never true for these operands (every product is >= 0)
 }
 
+// Issue-cost loops: each wave repeats one fixed group of instructions on eight rotating fp32
+// registers and independent accumulators, so (kinds 0-6) nothing waits on a recent result and the
+// time per group is what the instructions themselves cost the SIMD; kind 7 chains each multiply
+// into an exponential and pairs of those into a pack, as the prefill does per score. Wave 0 of each work-group records the shader-clock
+// cycles (s_memtime) and 100 MHz ticks (s_memrealtime) its loop took, from which the caller gets
+// the clock. The vector instructions are written as asm so the compiler neither folds nor reorders
+// them; they only read and write registers.
+#define SA_EXP(r) asm volatile("v_exp_f32 %0, %0" : "+v"(r))
+#define SA_MUL(r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(r) : "v"(k))
+#define SA_FMA(r) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(r) : "v"(k), "v"(k2))
+#define SA_CVT(d, a, b) asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b))
+#define SA_MFMA32(c) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0)
+#define SA_MFMA16(c) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0)
+#define SA_EXP8 SA_EXP(r0); SA_EXP(r1); SA_EXP(r2); SA_EXP(r3); SA_EXP(r4); SA_EXP(r5); SA_EXP(r6); SA_EXP(r7)
+#define SA_MUL8 SA_MUL(r0); SA_MUL(r1); SA_MUL(r2); SA_MUL(r3); SA_MUL(r4); SA_MUL(r5); SA_MUL(r6); SA_MUL(r7)
+#define SA_FMA8 SA_FMA(r0); SA_FMA(r1); SA_FMA(r2); SA_FMA(r3); SA_FMA(r4); SA_FMA(r5); SA_FMA(r6); SA_FMA(r7)
+#define SA_CVT8 SA_CVT(d0, r0, r1); SA_CVT(d1, r2, r3); SA_CVT(d2, r4, r5); SA_CVT(d3, r6, r7); \
+    SA_CVT(d0, r1, r0); SA_CVT(d1, r3, r2); SA_CVT(d2, r5, r4); SA_CVT(d3, r7, r6)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int kKind>
+__global__ __launch_bounds__(256) void issue_kernel(int iters, unsigned long long* clk, float* out) {
+    const float k = 0.9990234375f, k2 = 0.5f;
+    float r0 = threadIdx.x * 1e-3f, r1 = r0 + 1.0f, r2 = r0 + 2.0f, r3 = r0 + 3.0f, r4 = r0 - 1.0f,
+          r5 = r0 - 2.0f, r6 = r0 - 3.0f, r7 = r0 - 4.0f;
+    int d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = static_cast<__bf16>(static_cast<float>((threadIdx.x + e) & 7) * 0.125f);
+        b[e] = static_cast<__bf16>(static_cast<float>((threadIdx.x * 3 + e) & 7) * 0.0625f);
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    f32x4 s0 = {}, s1 = {};
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long q0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        if constexpr (kKind == 0) {  // 16 v_exp_f32
+            SA_EXP8; SA_EXP8;
+        } else if constexpr (kKind == 1) {  // 16 v_mul_f32
+            SA_MUL8; SA_MUL8;
+        } else if constexpr (kKind == 2) {  // 16 v_cvt_pk_bf16_f32
+            SA_CVT8; SA_CVT8;
+        } else if constexpr (kKind == 3) {  // 16 v_fma_f32
+            SA_FMA8; SA_FMA8;
+        } else if constexpr (kKind == 4) {  // 4 v_mfma_f32_32x32x16_bf16
+            SA_MFMA32(c0); SA_MFMA32(c1); SA_MFMA32(c2); SA_MFMA32(c3);
+        } else if constexpr (kKind == 5) {  // 4 v_mfma_f32_16x16x32_bf16
+            SA_MFMA16(s0); SA_MFMA16(s1); SA_MFMA16(s0); SA_MFMA16(s1);
+        } else if constexpr (kKind == 6) {  // 4 32x32x16 MFMAs, each followed by 4 exponentials
+            SA_MFMA32(c0); SA_EXP(r0); SA_EXP(r1); SA_EXP(r2); SA_EXP(r3);
+            SA_MFMA32(c1); SA_EXP(r4); SA_EXP(r5); SA_EXP(r6); SA_EXP(r7);
+            SA_MFMA32(c2); SA_EXP(r0); SA_EXP(r1); SA_EXP(r2); SA_EXP(r3);
+            SA_MFMA32(c3); SA_EXP(r4); SA_EXP(r5); SA_EXP(r6); SA_EXP(r7);
+        } else {  // a quarter of the prefill's per-tile mix: 8 + 2 MFMAs, 16 mul -> exp, 8 cvt
+            SA_MFMA32(c0); SA_MUL(r0); SA_EXP(r0); SA_MUL(r1); SA_EXP(r1);
+            SA_MFMA32(c1); SA_CVT(d0, r0, r1); SA_MUL(r2); SA_EXP(r2);
+            SA_MFMA32(c2); SA_MUL(r3); SA_EXP(r3); SA_CVT(d1, r2, r3);
+            SA_MFMA32(c3); SA_MUL(r4); SA_EXP(r4); SA_MUL(r5); SA_EXP(r5);
+            SA_MFMA16(s0); SA_CVT(d2, r4, r5); SA_MUL(r6); SA_EXP(r6);
+            SA_MFMA32(c0); SA_MUL(r7); SA_EXP(r7); SA_CVT(d3, r6, r7);
+            SA_MFMA32(c1); SA_MUL(r0); SA_EXP(r0); SA_MUL(r1); SA_EXP(r1);
+            SA_MFMA32(c2); SA_CVT(d0, r0, r1); SA_MUL(r2); SA_EXP(r2);
+            SA_MFMA32(c3); SA_MUL(r3); SA_EXP(r3); SA_CVT(d1, r2, r3);
+            SA_MFMA16(s1); SA_MUL(r4); SA_EXP(r4); SA_MUL(r5); SA_EXP(r5); SA_CVT(d2, r4, r5);
+            SA_MUL(r6); SA_EXP(r6); SA_MUL(r7); SA_EXP(r7); SA_CVT(d3, r6, r7);
+        }
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long q1 = __builtin_amdgcn_s_memrealtime();
+    float sum = r0 + r1 + r2 + r3 + r4 + r5 + r6 + r7 + static_cast<float>(d0 ^ d1 ^ d2 ^ d3) + s0[0] + s1[1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += c0[r] + c1[r] + c2[r] + c3[r];
+    if (sum == -12345.0f) out[0] = sum;  // keeps the results live
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = t1 - t0;
+        clk[2 * blockIdx.x + 1] = q1 - q0;
+    }
+}
+
+#undef SA_EXP8
+#undef SA_MUL8
+#undef SA_FMA8
+#undef SA_CVT8
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +168,25 @@ int sinkattn_ceiling_mfma_bf16(int blocks, int iters, void* out4, void* stream) 
 double sinkattn_ceiling_mfma_bf16_flop(int blocks, int iters) {
     // 4 waves per block, 4 MFMAs per iteration, 32 x 32 x 16 x 2 flop each.
     return static_cast<double>(blocks) * 4.0 * iters * 4.0 * 32.0 * 32.0 * 16.0 * 2.0;
+}
+
+int sinkattn_ceiling_issue(int kind, int blocks, int iters, void* clk, void* out4, void* stream) {
+    if (clk == nullptr || out4 == nullptr || blocks <= 0 || iters <= 0 || kind < 0 || kind > 7) return 1;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* c = static_cast<unsigned long long*>(clk);
+    auto* o = static_cast<float*>(out4);
+    switch (kind) {
+        case 0: issue_kernel<0><<<grid, block, 0, st>>>(iters, c, o); break;
+        case 1: issue_kernel<1><<<grid, block, 0, st>>>(iters, c, o); break;
+        case 2: issue_kernel<2><<<grid, block, 0, st>>>(iters, c, o); break;
+        case 3: issue_kernel<3><<<grid, block, 0, st>>>(iters, c, o); break;
+        case 4: issue_kernel<4><<<grid, block, 0, st>>>(iters, c, o); break;
+        case 5: issue_kernel<5><<<grid, block, 0, st>>>(iters, c, o); break;
+        case 6: issue_kernel<6><<<grid, block, 0, st>>>(iters, c, o); break;
+        default: issue_kernel<7><<<grid, block, 0, st>>>(iters, c, o); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 }  // extern "C"

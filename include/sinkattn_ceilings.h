@@ -1,10 +1,11 @@
 /* libsinkattn_ceilings: measured hardware ceilings, for reporting only.
  *
- * Two kernels that bound what the attention kernels of libsinkattn can reach on the GPU that runs
- * them: a streaming read of HBM (the bound of the split-KV decode, which reads every K/V byte once)
- * and a loop of bf16 matrix-core instructions (the bound of the prefill's two products). The
- * benchmark divides the attention kernels' rates by these measured rates, beside the published
- * peaks. Nothing in libsinkattn depends on this library.
+ * Kernels that bound what the attention kernels of libsinkattn can reach on the GPU that runs
+ * them: a streaming read of HBM (the bound of the split-KV decode, which reads every K/V byte once),
+ * a loop of bf16 matrix-core instructions (the bound of the prefill's two products), and loops of
+ * the prefill's inner-loop instructions that give what each costs a SIMD. The benchmark divides the
+ * attention kernels' rates by these measured rates, beside the published peaks. Nothing in
+ * libsinkattn depends on this library.
  *
  * Ownership and errors: the caller owns every buffer (device memory); the calls launch one kernel
  * on `stream` (a hipStream_t, NULL for the default stream), never synchronise, allocate nothing, and
@@ -30,6 +31,17 @@ int sinkattn_ceiling_mfma_bf16(int blocks, int iters, void* out4, void* stream);
 
 /* Floating-point operations of one sinkattn_ceiling_mfma_bf16(blocks, iters) launch. */
 double sinkattn_ceiling_mfma_bf16_flop(int blocks, int iters);
+
+/* `blocks` work-groups of four waves, each wave repeating `iters` times one group of instructions
+ * (independent of recent results except in kind 7), by `kind`: 0: 16 v_exp_f32; 1: 16 v_mul_f32;
+ * 2: 16 v_cvt_pk_bf16_f32; 3: 16 v_fma_f32; 4: 4 v_mfma_f32_32x32x16_bf16; 5: 4
+ * v_mfma_f32_16x16x32_bf16; 6: 4 of kind 4 with 4 v_exp_f32 after each; 7: 8
+ * v_mfma_f32_32x32x16_bf16, 2 v_mfma_f32_16x16x32_bf16, 16 v_exp_f32, 16 v_mul_f32 and 8
+ * v_cvt_pk_bf16_f32 interleaved, each exponential taking a product and each pack two exponentials
+ * (a quarter of a prefill tile's instructions per wave). `clk` is a device buffer of 2 x `blocks`
+ * uint64 that receives, per work-group, the shader-clock cycles (s_memtime) and 100 MHz ticks
+ * (s_memrealtime) of wave 0's loop. `out4` as above. */
+int sinkattn_ceiling_issue(int kind, int blocks, int iters, void* clk, void* out4, void* stream);
 
 #ifdef __cplusplus
 }

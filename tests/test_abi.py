@@ -69,7 +69,7 @@ def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
     text = open(CEILINGS_HEADER).read()
     names = set(re.findall(r"^\s*(?:int|double)\s+(sinkattn_ceiling_\w+)\s*\(", text, flags=re.M))
     assert names == {"sinkattn_ceiling_stream_read", "sinkattn_ceiling_mfma_bf16",
-                     "sinkattn_ceiling_mfma_bf16_flop"}
+                     "sinkattn_ceiling_mfma_bf16_flop", "sinkattn_ceiling_issue"}
     lib = ctypes.CDLL(CEILINGS_LIB)
     for name in names:
         assert hasattr(lib, name), name
@@ -85,6 +85,13 @@ def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
     assert lib.sinkattn_ceiling_stream_read(fake, 1 << 20, 0, fake, None) == 1
     assert lib.sinkattn_ceiling_mfma_bf16(0, 10, fake, None) == 1
     assert lib.sinkattn_ceiling_mfma_bf16(8, 0, fake, None) == 1
+    lib.sinkattn_ceiling_issue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.sinkattn_ceiling_issue(8, 8, 10, fake, fake, None) == 1   # no such kind
+    assert lib.sinkattn_ceiling_issue(-1, 8, 10, fake, fake, None) == 1
+    assert lib.sinkattn_ceiling_issue(0, 0, 10, fake, fake, None) == 1
+    assert lib.sinkattn_ceiling_issue(0, 8, 0, fake, fake, None) == 1
+    assert lib.sinkattn_ceiling_issue(0, 8, 10, None, fake, None) == 1
     # 4 waves x 4 MFMAs of 32 x 32 x 16 x 2 flop per block and iteration.
     assert lib.sinkattn_ceiling_mfma_bf16_flop(3, 5) == 3 * 5 * 4 * 4 * 32 * 32 * 16 * 2
 

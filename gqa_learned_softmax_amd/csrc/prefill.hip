@@ -703,7 +703,45 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
     if (redo_general) process(False());
 
     // Epilogue: out = acc / d. Lane holds d-channels 32n + 8 (r / 4) + 4 half + r % 4.
+    // bf16 output goes through LDS: each wave writes its 64 rows x 64 d row-major into one of the
+    // K/V buffers (free once every wave is past its last tile; 16-byte chunk c of row r at
+    // c ^ (r & 7), so both the 8-byte writes and the 16-byte reads are conflict-free), then stores
+    // whole 128-byte rows, eight lanes per row: the rows of one position's heads are adjacent in
+    // memory, so every store instruction writes full lines instead of 16 bytes of 32 rows.
     // Split-KV prefill writes the split's state instead: o = acc / d, m (natural log), d.
+    if constexpr (!kSplit) {
+        if (p.out_is_bf16) {
+            if (redo_general) __syncthreads();  // the second pass ends without a barrier
+            __bf16* stage = wave < kStages ? k_lds[wave] : v_lds[wave - kStages];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const float dtot = sum_xor32(dsum[cb]);
+                const float inv = dtot > 0.0f ? 1.0f / dtot : 0.0f;
+                const int row = cb * 32 + col;
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int quad = 0; quad < 4; ++quad) {
+                        bf16x4 o;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[cb][n][4 * quad + i] * inv);
+                        *reinterpret_cast<bf16x4*>(&stage[row * 64 + 8 * ((4 * n + quad) ^ (row & 7)) + 4 * half]) = o;
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 8 * j + (lane >> 3), c = lane & 7;
+                const bf16x8 o = *reinterpret_cast<const bf16x8*>(&stage[row * 64 + 8 * (c ^ (row & 7))]);
+                const int r = wave * kRowsPerWave + row;
+                const int rpos = first_pos + r / group;
+                if (rpos >= q_len) continue;
+                *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) +
+                                           static_cast<int64_t>(q_start + rpos) * p.o_stride_tok +
+                                           static_cast<int64_t>(g * group + r % group) * p.o_stride_head + 8 * c) = o;
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
         const float dtot = sum_xor32(dsum[cb]);

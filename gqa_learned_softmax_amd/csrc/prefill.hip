@@ -704,10 +704,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
 
     // Epilogue: out = acc / d. Lane holds d-channels 32n + 8 (r / 4) + 4 half + r % 4.
     // bf16 output goes through LDS: each wave writes its 64 rows x 64 d row-major into one of the
-    // K/V buffers (free once every wave is past its last tile; 16-byte chunk c of row r at
-    // c ^ (r & 7), so both the 8-byte writes and the 16-byte reads are conflict-free), then stores
-    // whole 128-byte rows, eight lanes per row: the rows of one position's heads are adjacent in
-    // memory, so every store instruction writes full lines instead of 16 bytes of 32 rows.
+    // K/V buffers (free once every wave is past its last tile), then stores whole 128-byte rows,
+    // eight lanes per row: the rows of one position's heads are adjacent in memory, so every store
+    // instruction writes full lines instead of 16 bytes of 32 rows. 16-byte chunk c of row r sits
+    // at c ^ (r & 7), its two 8-byte halves swapped when r & 8: the 8-byte writes of 16 rows and
+    // the 16-byte reads of 8 rows then hit distinct banks.
     // Split-KV prefill writes the split's state instead: o = acc / d, m (natural log), d.
     if constexpr (!kSplit) {
         if (p.out_is_bf16) {
@@ -725,13 +726,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_bf16_kernel(PrefillPara
                         bf16x4 o;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[cb][n][4 * quad + i] * inv);
-                        *reinterpret_cast<bf16x4*>(&stage[row * 64 + 8 * ((4 * n + quad) ^ (row & 7)) + 4 * half]) = o;
+                        *reinterpret_cast<bf16x4*>(
+                            &stage[row * 64 + 8 * ((4 * n + quad) ^ (row & 7)) + 4 * (half ^ ((row >> 3) & 1))]) = o;
                     }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int row = 8 * j + (lane >> 3), c = lane & 7;
-                const bf16x8 o = *reinterpret_cast<const bf16x8*>(&stage[row * 64 + 8 * (c ^ (row & 7))]);
+                bf16x8 o = *reinterpret_cast<const bf16x8*>(&stage[row * 64 + 8 * (c ^ (row & 7))]);
+                if (j & 1) o = __builtin_shufflevector(o, o, 4, 5, 6, 7, 0, 1, 2, 3);  // row & 8: halves swapped
                 const int r = wave * kRowsPerWave + row;
                 const int rpos = first_pos + r / group;
                 if (rpos >= q_len) continue;

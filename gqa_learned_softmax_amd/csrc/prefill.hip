@@ -22,8 +22,9 @@
 //   O^T (64 d x 64 rows) += V^T . P^T: 16 MFMA. The S^T accumulator lanes are exactly the P^T
 //     operand lanes, so P never leaves registers; V stays row-major in LDS and comes back
 //     transposed through ds_read_b64_tr_b16.
-// K/V tiles are double-buffered in LDS: the next tile's buffer loads are issued before the
-// current tile's math and written to the other buffer after it, one barrier per tile.
+// K/V tiles go from memory straight into three LDS buffers (buffer_load ... lds), two tiles
+// ahead of the one being multiplied, one barrier per tile. The bf16 output leaves through LDS as
+// whole 128-byte rows.
 // Work-groups are numbered query-tile-major with the KV head fastest, so consecutive
 // work-groups (which the dispatcher spreads over the eight XCDs) read different KV heads and each
 // XCD's L2 keeps re-serving one head's K/V. Within a sequence, tiles are issued last-position

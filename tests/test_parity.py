@@ -159,6 +159,8 @@ PREFILL_SMALL = [
     # More sequences than a wave has lanes: the tile search takes two and three 64-way steps.
     ("many_seqs_100", [(i * 37) % 71 for i in range(100)], None, 64, 8, True, (-2, 2)),
     ("many_seqs_4500", [(i * 7) % 5 for i in range(4500)], None, 16, 8, True, (-2, 2)),
+    ("seqs_64", [(i * 29) % 40 + 1 for i in range(64)], None, 64, 8, True, (-2, 2)),
+    ("seqs_65", [(i * 29) % 40 + 1 for i in range(65)], None, 64, 8, True, (-2, 2)),
 ]
 
 
@@ -330,6 +332,10 @@ DECODE_SMALL = [
     ("quad_heads", [(37 * i) % 513 for i in range(32)], 512, 8, 64, 8, (-2, 2), 0.0),
     # 1 x 8 x 20 = 160 work-groups: one round, so sinkattn_decode merges more than 16 chunks in its tail
     ("many_chunks_one_round", [1000], 1024, 20, 64, 8, (-2, 2), 0.0),
+    # More than one round of work-groups, whose (sequence, head set) index is rotated by the chunk,
+    # with 12 and 15 rows per chunk (not multiples of the eight XCDs)
+    ("rotated_paired_r12", [900, 17, 480], 960, 30, 64, 8, (-2, 2), 0.0),
+    ("rotated_single_r15", [300, 0, 77, 299, 150], 320, 20, 12, 3, (-2, 2), 0.0),
 ]
 
 

@@ -405,42 +405,40 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
     }
 
     if constexpr (kKeySplit) {
-        // Combine the team's four states in the (now free) V tiles: per KV head, m and d of each
-        // wave's 16 columns, then each wave's O^T (64 d x 16 columns); wave 0 rescales them to the
-        // common maximum and sums.
-        constexpr int kStateFloats = 4 * 16 * 2 + 4 * kHeadDim * 16;
+        // Combine the team's four states in the (now free) V tiles, a quarter of O^T per wave:
+        // every wave publishes m and d of its 16 columns and its four 16-row blocks of O^T; wave w
+        // then rescales block w of all four states to the common maximum and sums them, so it
+        // holds rows [16w, 16w + 16) of each column's combined O^T in acc[0], and every wave the
+        // combined d (on group 0, as the fold keeps it) and m.
+        constexpr int kStateFloats = 4 * 16 * 2 + 4 * 4 * 64 * 4;
         static_assert(sizeof(v_lds) >= sizeof(float) * kHeads * kStateFloats, "state space");
         float* st = reinterpret_cast<float*>(&v_lds[0][0][0][0]) + hsub * kStateFloats;
+        f32x4* parts = reinterpret_cast<f32x4*>(st + 4 * 16 * 2);
         const float d_wave = sum_over_groups(dsum);
-        if (grp == 0) {
-            st[16 * tile + col] = m;
-            st[64 + 16 * tile + col] = d_wave;
-        }
+        if (grp == 0) *reinterpret_cast<f32x2*>(&st[2 * (16 * tile + col)]) = f32x2{m, d_wave};
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st[128 + (tile * kHeadDim + 16 * n + 4 * grp + i) * 16 + col] = acc[n][i];
+        for (int n = 0; n < 4; ++n) parts[(4 * n + tile) * 64 + lane] = acc[n];
         __syncthreads();
-        if (tile == 0) {
-            float big = kNegInf;
+        float mw[4], dw[4];
+        float big = kNegInf;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) big = fmaxf(big, st[16 * w + col]);
-            float d_all = 0.0f;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) acc[n] = zero_f32x4();
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float mw = st[16 * w + col];
-                const float sc = mw == kNegInf ? 0.0f : exp2_fast(mw - big);
-                d_all += st[64 + 16 * w + col] * sc;
-#pragma unroll
-                for (int n = 0; n < 4; ++n)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[n][i] += sc * st[128 + (w * kHeadDim + 16 * n + 4 * grp + i) * 16 + col];
-            }
-            m = big;
-            dsum = grp == 0 ? d_all : 0.0f;
+        for (int w = 0; w < 4; ++w) {
+            const f32x2 md = *reinterpret_cast<const f32x2*>(&st[2 * (16 * w + col)]);
+            mw[w] = md[0];
+            dw[w] = md[1];
+            big = fmaxf(big, mw[w]);
         }
+        float d_all = 0.0f;
+        f32x4 o = zero_f32x4();
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float sc = mw[w] == kNegInf ? 0.0f : exp2_fast(mw[w] - big);
+            d_all += dw[w] * sc;
+            o += sc * parts[(4 * tile + w) * 64 + lane];
+        }
+        acc[0] = o;
+        m = big;
+        dsum = grp == 0 ? d_all : 0.0f;
     }
 
     // The chunk state of each valid column: o = acc / d, m (natural log), d.
@@ -457,11 +455,14 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
         static_assert(sizeof(k_lds) >= sizeof(float) * kWaves * 16 * (kOPitch + 2), "staging space");
         float (*ot_all)[kOPitch] = reinterpret_cast<float (*)[kOPitch]>(&k_lds[0][0][0][0]);
         float* md_all = reinterpret_cast<float*>(&k_lds[0][0][0][0]) + kWaves * 16 * kOPitch;
-        if (writes_state) {
-            float (*ot)[kOPitch] = ot_all + 16 * wave_all;
+        if (kKeySplit || writes_state) {
+            float (*ot)[kOPitch] = ot_all + 16 * (kKeySplit ? hsub * kSplitWaves : wave_all);
+            if constexpr (kKeySplit)
+                *reinterpret_cast<f32x4*>(&ot[col][16 * tile + 4 * grp]) = acc[0] * inv;
+            else
 #pragma unroll
-            for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(&ot[col][16 * n + 4 * grp]) = acc[n] * inv;
-            if (grp == 0) {
+                for (int n = 0; n < 4; ++n) *reinterpret_cast<f32x4*>(&ot[col][16 * n + 4 * grp]) = acc[n] * inv;
+            if (writes_state && grp == 0) {
                 md_all[(2 * wave_all) * 16 + col] = m_nat;
                 md_all[(2 * wave_all + 1) * 16 + col] = d_tot;
             }
@@ -503,6 +504,12 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
                                        __HIP_MEMORY_SCOPE_SYSTEM);
                 }
             }
+        }
+    } else if (kKeySplit && col_valid) {
+        *reinterpret_cast<f32x4*>(p.partial_o + row * kHeadDim + 16 * tile + 4 * grp) = acc[0] * inv;
+        if (tile == 0 && grp == 0) {
+            p.partial_m[row] = m_nat;
+            p.partial_d[row] = d_tot;
         }
     } else if (writes_state && col_valid) {
         float* orow = p.partial_o + row * kHeadDim + 4 * grp;

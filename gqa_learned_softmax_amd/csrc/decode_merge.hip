@@ -44,10 +44,20 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_x4_kernel(Decod
         p.lse[b * p.lse_stride_b + tok * p.lse_stride_tok + h * p.lse_stride_head] = lse;
 }
 
+// One row per wave. Work-group order: work-groups go to the eight XCDs round-robin by index, and
+// when the rows come in whole groups of 8 blocks of 16, work-group w merges quarter (w / 8) % 4 of
+// 16-row block 8 (w / 32) + w % 8, so block j is merged on XCD j mod 8. A split launch of a single
+// round whose work-groups each cover 16 consecutive rows (two KV heads of a group of 8, one token)
+// writes block j's chunk states from XCD j mod 8 too, and the merge then reads them from that XCD's
+// L2 (8 x 8192 keys, 64/8 heads: split + merge 27.05 instead of 27.5 us, same machine). For other
+// split layouts this order is as good as the plain one.
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeMergeParams p) {
+    static_assert(kMergeWaves == 4, "four work-groups per 16-row block");
     const int lane = threadIdx.x & 63;
-    const int64_t bh = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
-    if (bh >= static_cast<int64_t>(p.batch) * p.num_q_heads) return;
+    const int64_t rows = static_cast<int64_t>(p.batch) * p.num_q_heads;
+    const int64_t w = blockIdx.x;
+    const int64_t bh = (rows % 128 == 0 ? 16 * (8 * (w / 32) + w % 8) + 4 * ((w / 8) % 4) : 4 * w) + (threadIdx.x >> 6);
+    if (bh >= rows) return;
     const int64_t bt = bh / p.num_q_heads;
     const int b = static_cast<int>(bt / p.q_len);
     const int tok = static_cast<int>(bt % p.q_len);

@@ -48,9 +48,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_x4_kernel(Decod
 // when the rows come in whole groups of 8 blocks of 16, work-group w merges quarter (w / 8) % 4 of
 // 16-row block 8 (w / 32) + w % 8, so block j is merged on XCD j mod 8. A split launch of a single
 // round whose work-groups each cover 16 consecutive rows (two KV heads of a group of 8, one token)
-// writes block j's chunk states from XCD j mod 8 too, and the merge then reads them from that XCD's
-// L2 (8 x 8192 keys, 64/8 heads: split + merge 27.05 instead of 27.5 us, same machine). For other
-// split layouts this order is as good as the plain one.
+// writes block j's chunk states from XCD j mod 8 too, so each block is merged on the XCD that wrote
+// it: 8 x 8192 keys, 64/8 heads, split + merge 26.5 instead of 27.2 us (same machine). The merge's
+// L2 misses (FETCH_SIZE) are the same in either order, so the states do not come from that L2; why
+// the aligned order is faster is not established. For other split layouts this order is as good as
+// the plain one.
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeMergeParams p) {
     static_assert(kMergeWaves == 4, "four work-groups per 16-row block");
     const int lane = threadIdx.x & 63;

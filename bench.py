@@ -195,6 +195,22 @@ def measure_ceilings(torch, dev):
         best = max(best, (part / (ms * 1e-3) / 1e9, blocks))
     res["stream_read_128MiB_gbs"] = round(best[0], 1)
     res["stream_read_128MiB_blocks"] = best[1]
+    # The decode workload's own read pattern (8 sequences x 8 chunks of 1024 rows of 1 KB in K and in
+    # V, 256-byte slices, 256 work-groups of 512 threads), rotating through the same buffer.
+    lib.sinkattn_ceiling_stream_read_slices.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+
+    def slices(base):
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+        rc = lib.sinkattn_ceiling_stream_read_slices(ctypes.c_void_p(base), ctypes.c_void_p(base + part // 2), 8, 8,
+                                                     1024, 1024, ctypes.c_void_p(sink.data_ptr()),
+                                                     ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"slice-read ceiling launch failed ({rc})")
+
+    ms = _time_graph(_capture(lambda i: slices(buf.data_ptr() + (i % n_parts) * part), 48, torch), 48, torch,
+                     replays=5)
+    res["stream_read_decode_slices_gbs"] = round(part / (ms * 1e-3) / 1e9, 1)
     del buf
 
     def mfma(blocks, iters):
@@ -495,6 +511,9 @@ def main():
             "measured_stream_read_gbs": ceilings["stream_read_128MiB_gbs"] if ceilings else None,
             "frac_of_measured_stream_read": (round(split_gbs / ceilings["stream_read_128MiB_gbs"], 4)
                                              if ceilings else None),
+            "measured_decode_slices_read_gbs": ceilings["stream_read_decode_slices_gbs"] if ceilings else None,
+            "frac_of_measured_decode_slices_read": (round(split_gbs / ceilings["stream_read_decode_slices_gbs"], 4)
+                                                    if ceilings else None),
         },
         "ceilings": ceilings,
         "decode_detail": {
@@ -510,6 +529,8 @@ def main():
             "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
             "step_frac_of_measured_stream_read": (round(value / ceilings["stream_read_128MiB_gbs"], 4)
                                                   if ceilings else None),
+            "step_frac_of_measured_decode_slices_read": (
+                round(value / ceilings["stream_read_decode_slices_gbs"], 4) if ceilings else None),
         },
     }
 

@@ -37,6 +37,37 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
     if (x == 0x9E3779B9u) out[0] = x;
 }
 
+// The split-KV decode's read pattern with nothing else: two row-major tensors (a token-major K and V
+// cache) of seqs x chunks x rows_per_chunk rows, every 256-byte slice of every row read once with
+// non-temporal 16-byte loads. Work-group w takes slice w % S (S = row_pieces / 16) of the rows of
+// chunk g / seqs of sequence g % seqs, g = w / S (the decode's order: KV-head pair fastest, then the
+// sequence, then the chunk); its 512 threads read pieces j = tid + 512 u of the chunk's slice (16
+// per row), two of K and two of V in flight per thread.
+__global__ __launch_bounds__(512) void stream_read_slices_kernel(const u32x4* __restrict__ k,
+                                                                 const u32x4* __restrict__ v, uint32_t row_pieces,
+                                                                 uint32_t seqs, uint32_t chunks,
+                                                                 uint32_t rows_per_chunk, uint32_t* out) {
+    const uint32_t slices = row_pieces / 16;
+    const uint32_t w = blockIdx.x;
+    const uint32_t slice = w % slices;
+    const uint32_t g = w / slices;
+    const uint64_t row0 = (static_cast<uint64_t>(g % seqs) * chunks + g / seqs) * rows_per_chunk;
+    const uint32_t pieces = rows_per_chunk * 16;
+    auto at = [&](uint32_t j) { return (row0 + j / 16) * row_pieces + slice * 16 + j % 16; };
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    uint32_t j = threadIdx.x;
+    for (; j + 512 < pieces; j += 1024) {
+        const u32x4 a = __builtin_nontemporal_load(k + at(j));
+        const u32x4 b = __builtin_nontemporal_load(k + at(j + 512));
+        const u32x4 c = __builtin_nontemporal_load(v + at(j));
+        const u32x4 d = __builtin_nontemporal_load(v + at(j + 512));
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; j < pieces; j += 512) acc ^= __builtin_nontemporal_load(k + at(j)) ^ __builtin_nontemporal_load(v + at(j));
+    const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == 0x9E3779B9u) out[0] = x;
+}
+
 // Four independent accumulation chains of v_mfma_f32_32x32x16_bf16 per wave, so consecutive MFMAs
 // never wait on each other's results; operands come from the thread index so nothing folds away.
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* out) {
@@ -155,6 +186,23 @@ int sinkattn_ceiling_stream_read(const void* buf, uint64_t bytes, int blocks, vo
         return 1;
     stream_read_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
         static_cast<const u32x4*>(buf), bytes / 16, static_cast<uint32_t*>(out4));
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int sinkattn_ceiling_stream_read_slices(const void* k, const void* v, int seqs, int chunks, int rows_per_chunk,
+                                        int row_bytes, void* out4, void* stream) {
+    if (k == nullptr || v == nullptr || out4 == nullptr || seqs <= 0 || chunks <= 0 || rows_per_chunk <= 0 ||
+        row_bytes <= 0 || row_bytes % 256 != 0 || reinterpret_cast<uintptr_t>(k) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(v) % 16 != 0)
+        return 1;
+    const int64_t groups = static_cast<int64_t>(seqs) * chunks * (row_bytes / 256);
+    const int64_t rows = static_cast<int64_t>(seqs) * chunks * rows_per_chunk;
+    if (groups > 0x7FFFFFFF || static_cast<int64_t>(rows_per_chunk) * 16 > 0x7FFFFFFF || rows > (int64_t(1) << 40))
+        return 1;
+    stream_read_slices_kernel<<<dim3(static_cast<unsigned>(groups)), dim3(512), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), static_cast<uint32_t>(row_bytes / 16),
+        static_cast<uint32_t>(seqs), static_cast<uint32_t>(chunks), static_cast<uint32_t>(rows_per_chunk),
+        static_cast<uint32_t*>(out4));
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -25,6 +25,15 @@ extern "C" {
  * pointer to 4 writable bytes that the kernel writes only for a fill pattern no caller uses. */
 int sinkattn_ceiling_stream_read(const void* buf, uint64_t bytes, int blocks, void* out4, void* stream);
 
+/* The split-KV decode's read pattern alone: `k` and `v` (device, 16-byte aligned) each hold
+ * seqs x chunks x rows_per_chunk rows of `row_bytes` bytes (a multiple of 256), row-major; every
+ * 256-byte slice of every row of both is read once with non-temporal 16-byte loads, by
+ * seqs x chunks x (row_bytes / 256) work-groups of 512 threads, one per (slice, sequence, chunk)
+ * numbered slice fastest, then sequence, then chunk (the decode kernel's order for pairs of KV heads
+ * of 128 bytes each). `out4` as above. */
+int sinkattn_ceiling_stream_read_slices(const void* k, const void* v, int seqs, int chunks, int rows_per_chunk,
+                                        int row_bytes, void* out4, void* stream);
+
 /* `blocks` work-groups of four waves, each wave issuing `iters` x 4 independent
  * v_mfma_f32_32x32x16_bf16; `out4` as above. */
 int sinkattn_ceiling_mfma_bf16(int blocks, int iters, void* out4, void* stream);

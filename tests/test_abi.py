@@ -68,7 +68,7 @@ def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
     rejects invalid arguments on the host (return 1) without launching anything."""
     text = open(CEILINGS_HEADER).read()
     names = set(re.findall(r"^\s*(?:int|double)\s+(sinkattn_ceiling_\w+)\s*\(", text, flags=re.M))
-    assert names == {"sinkattn_ceiling_stream_read", "sinkattn_ceiling_mfma_bf16",
+    assert names == {"sinkattn_ceiling_stream_read", "sinkattn_ceiling_stream_read_slices", "sinkattn_ceiling_mfma_bf16",
                      "sinkattn_ceiling_mfma_bf16_flop", "sinkattn_ceiling_issue"}
     lib = ctypes.CDLL(CEILINGS_LIB)
     for name in names:
@@ -89,6 +89,15 @@ def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
                                            ctypes.c_void_p, ctypes.c_void_p]
     assert lib.sinkattn_ceiling_issue(8, 8, 10, fake, fake, None) == 1   # no such kind
     assert lib.sinkattn_ceiling_issue(-1, 8, 10, fake, fake, None) == 1
+    lib.sinkattn_ceiling_stream_read_slices.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sl = lib.sinkattn_ceiling_stream_read_slices
+    assert sl(None, fake, 8, 8, 1024, 1024, fake, None) == 1
+    assert sl(fake, fake + 8, 8, 8, 1024, 1024, fake, None) == 1     # misaligned V
+    assert sl(fake, fake, 8, 8, 1024, 1000, fake, None) == 1         # rows not whole 256-byte slices
+    assert sl(fake, fake, 0, 8, 1024, 1024, fake, None) == 1
+    assert sl(fake, fake, 8, 8, 0, 1024, fake, None) == 1
+    assert sl(fake, fake, 8, 8, 1024, 1024, None, None) == 1
     assert lib.sinkattn_ceiling_issue(0, 0, 10, fake, fake, None) == 1
     assert lib.sinkattn_ceiling_issue(0, 8, 0, fake, fake, None) == 1
     assert lib.sinkattn_ceiling_issue(0, 8, 10, None, fake, None) == 1

@@ -62,6 +62,7 @@ inline const char* bool_name(bool x) { return x ? "true" : "false"; }
 struct DecodeShape {
     int heads;       // KV heads per work-group: 1, 2 or 4
     bool key_split;  // the waves of a KV head split the keys (G x T <= 16)
+    bool private_staging;  // each wave stages only its own keys' rows, no barrier per block
     int64_t groups;  // work-groups in the grid
     int block;       // threads per work-group
 };
@@ -84,6 +85,10 @@ inline DecodeShape decode_shape(const DecodeSplitParams& p) {
         s.groups = static_cast<int64_t>(p.batch) * p.num_kv_heads * p.num_chunks;
     }
     s.block = s.heads * kSplitThreads;
+    // Private staging where it was measured faster: pairs of KV heads, key split, a single round of
+    // work-groups (8 x 8192 keys: split + merge 26.0 vs 27.1 us); the multi-round grids of four
+    // heads were 7-8% slower with it.
+    s.private_staging = s.heads == 2 && s.key_split && s.groups <= kComputeUnits;
     return s;
 }
 
@@ -98,8 +103,8 @@ inline bool decode_fused_fits_one_round(const DecodeSplitParams& p) {
 inline Launch plan_decode_split_bf16(const DecodeSplitParams& p, bool fused) {
     const DecodeShape s = decode_shape(p);
     char name[96];
-    snprintf(name, sizeof(name), "decode_split_bf16_kernel<%d, %s, %s>", s.heads, bool_name(fused),
-             bool_name(s.key_split));
+    snprintf(name, sizeof(name), "decode_split_bf16_kernel<%d, %s, %s, %s>", s.heads, bool_name(fused),
+             bool_name(s.key_split), bool_name(s.private_staging));
     return make_launch(name, s.groups, s.block);
 }
 

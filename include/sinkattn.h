@@ -377,7 +377,7 @@ sinkattn_status sinkattn_linear_fp8_block_scaled(const sinkattn_tensor* x, const
  * right alignment do. Nothing is launched, allocated or synchronised.
  *
  *   kernel   the kernel's name as a profiler prints it, without namespace or parameter list
- *            (template arguments included, e.g. "decode_split_bf16_kernel<2, false, true>")
+ *            (template arguments included, e.g. "decode_split_bf16_kernel<2, false, true, true>")
  *   grid     work-groups of the launch
  *   block    threads per work-group
  */

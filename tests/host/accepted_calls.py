@@ -109,6 +109,11 @@ def expected_shape(b, hq, hkv, chunks, q_len, adjacent):
     return heads, (hq // hkv) * q_len <= 16, groups
 
 
+def expected_private(heads, key_split, groups):
+    """Private per-wave staging: pairs of KV heads, key split, a single round of work-groups."""
+    return heads == 2 and key_split and groups <= COMPUTE_UNITS
+
+
 SPLIT_CASES = [
     # name, B, Hq, Hkv, capacity, chunks, T, head-major cache
     ("decode_8x8192", 8, 64, 8, 8192, 8, 1, False),
@@ -136,7 +141,10 @@ def test_decode_split_launch(name, b, hq, hkv, cap, chunks, t, hm):
     assert r["launcher"] == "decode_split_bf16"
     assert (r["heads_per_group"], r["key_split"], r["grid"]) == (heads, key_split, groups)
     assert r["block"] == 256 * heads
-    assert r["kernel"] == f"decode_split_bf16_kernel<{heads}, false, {str(key_split).lower()}>"
+    priv = expected_private(heads, key_split, groups)
+    assert r["private_staging"] == priv
+    assert r["kernel"] == (f"decode_split_bf16_kernel<{heads}, false, {str(key_split).lower()}, "
+                           f"{str(priv).lower()}>")
     assert r["chunk_size"] == math.ceil(cap / chunks) and r["capacity"] == cap
     assert (r["batch"], r["q_len"], r["num_chunks"]) == (b, t, chunks)
     assert (r["partial_o"], r["partial_m"], r["partial_d"]) == (po.data, pm.data, pd.data)
@@ -145,9 +153,9 @@ def test_decode_split_launch(name, b, hq, hkv, cap, chunks, t, hm):
 
 
 def test_decode_split_grid_of_the_known_workloads():
-    expect = {"decode_8x8192": ("decode_split_bf16_kernel<2, false, true>", 256, 512),
-              "long_decode_32x32768": ("decode_split_bf16_kernel<4, false, true>", 1024, 1024),
-              "mixed_decode_128x8192": ("decode_split_bf16_kernel<4, false, true>", 2048, 1024)}
+    expect = {"decode_8x8192": ("decode_split_bf16_kernel<2, false, true, true>", 256, 512),
+              "long_decode_32x32768": ("decode_split_bf16_kernel<4, false, true, false>", 1024, 1024),
+              "mixed_decode_128x8192": ("decode_split_bf16_kernel<4, false, true, false>", 2048, 1024)}
     for name, b, hq, hkv, cap, chunks, t, hm in SPLIT_CASES:
         if name in expect:
             recs, _, _ = split_call(b, hq, hkv, cap, chunks, t, head_major=hm)
@@ -192,7 +200,8 @@ def test_decode_single_launch_decision_and_workspace(name, b, hq, hkv, cap, chun
     one_round = dt == BF16 and groups <= COMPUTE_UNITS
     if one_round:
         assert [r["launcher"] for r in recs] == ["decode_fused_bf16"]
-        assert recs[0]["kernel"] == f"decode_split_bf16_kernel<{heads}, true, {str(key_split).lower()}>"
+        priv = str(expected_private(heads, key_split, groups)).lower()
+        assert recs[0]["kernel"] == f"decode_split_bf16_kernel<{heads}, true, {str(key_split).lower()}, {priv}>"
         assert recs[0]["counters"] == ws + counters
         assert (recs[0]["out"], recs[0]["lse"]) == (out.data, lse.data)
     else:

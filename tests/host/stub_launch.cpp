@@ -56,12 +56,12 @@ std::string launch_fields(const sinkattn::Launch& l) {
 
 hipError_t record_decode(const char* launcher, const sinkattn::DecodeSplitParams& p, const sinkattn::Launch& l) {
     const sinkattn::DecodeShape s = sinkattn::decode_shape(p);
-    append(fmt("{\"launcher\": \"%s\", %s, \"heads_per_group\": %d, \"key_split\": %s, \"batch\": %d, "
+    append(fmt("{\"launcher\": \"%s\", %s, \"heads_per_group\": %d, \"key_split\": %s, \"private_staging\": %s, \"batch\": %d, "
                "\"q_len\": %d, \"num_q_heads\": %d, \"num_kv_heads\": %d, \"num_chunks\": %d, "
                "\"capacity\": %lld, \"chunk_size\": %lld, \"k_stride_head\": %lld, \"partial_o\": %llu, "
                "\"partial_m\": %llu, \"partial_d\": %llu, \"counters\": %llu, \"out\": %llu, \"lse\": %llu, "
                "\"out_is_bf16\": %d}",
-               launcher, launch_fields(l).c_str(), s.heads, s.key_split ? "true" : "false", p.batch, p.q_len,
+               launcher, launch_fields(l).c_str(), s.heads, s.key_split ? "true" : "false", s.private_staging ? "true" : "false", p.batch, p.q_len,
                p.num_q_heads, p.num_kv_heads, p.num_chunks, static_cast<long long>(p.capacity),
                static_cast<long long>(p.chunk_size), static_cast<long long>(p.k_stride_head), addr(p.partial_o),
                addr(p.partial_m), addr(p.partial_d), addr(p.counters), addr(p.out), addr(p.lse), p.out_is_bf16));

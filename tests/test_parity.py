@@ -327,6 +327,9 @@ DECODE_SMALL = [
     ("odd_kv_heads", [300, 77], 320, 4, 12, 3, (-2, 2), 0.0),
     # B * Hkv/2 * C = 256 with a token-major cache: the two-KV-heads-per-work-group kernel
     ("paired_heads", [250, 3, 0, 129], 256, 16, 64, 8, (-2, 2), 0.0),
+    # 8 x 4 x 8 = 256 paired work-groups of 1024-key chunks: one round, so each wave stages its own
+    # keys' rows (private staging); lengths end inside blocks, on block borders and at zero
+    ("paired_private_ragged", [8191, 4097, 1, 0, 2048, 6000, 63, 65], 8192, 8, 64, 8, (-2, 2), 0.0),
     ("single_kv_head", [500, 64], 512, 3, 16, 1, (-2, 2), 0.0),
     # B * Hkv/4 * C = 512 with a token-major cache: the four-KV-heads-per-work-group kernel
     ("quad_heads", [(37 * i) % 513 for i in range(32)], 512, 8, 64, 8, (-2, 2), 0.0),
@@ -544,7 +547,7 @@ def test_merge_many_rows_random_states(chunks, out_dtype):
 # ----------------------------------------------------------------------------- fused split + merge
 FUSED_CASES = [c for c in DECODE_SMALL if c[0] in
                ("uniform", "ragged_empty_chunks", "many_chunks", "group16", "outliers", "odd_kv_heads",
-                "single_kv_head", "paired_heads", "quad_heads", "kv_len_1", "weak_sinks",
+                "single_kv_head", "paired_heads", "paired_private_ragged", "quad_heads", "kv_len_1", "weak_sinks",
                 "many_chunks_one_round")]
 
 

@@ -25,6 +25,9 @@
 // waves split each block's keys instead (fold_keys) and combine their states at the chunk end. The
 // loads of block i + 2 are in flight while block i is folded and block i + 1 goes from registers
 // into the other LDS buffer; one barrier per block. (One block ahead, or three, measured slower.)
+// On a single round of paired work-groups with the key split, each wave instead loads and stages
+// only its own 16 keys' rows of its own head in a private LDS region, so the loop has no barrier
+// (private staging, below).
 //
 // With T tokens, the sequence length L counts the new tokens, and token t sees keys j <= L - T + t
 // (the causal rule of the last T rows of a prefill); only the last T - 1 keys need a mask.

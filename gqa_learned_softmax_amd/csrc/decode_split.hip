@@ -402,9 +402,9 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
         // chunk c of row r at position c ^ ((r >> 1) & 7) for K (the 16 rows' operand reads hit 16
         // different bank groups) and c ^ (((r >> 1) & 3) << 1) for V (the transpose reads of 8 rows
         // by two chunks likewise). Measured on 8 x 8192 keys against the shared staging below:
-        // split + merge 25.9-26.2 vs 27.1 us; on the multi-round grids of four heads it was 7-8%
-        // slower (the shared staging reads 512 contiguous bytes of each row per instruction), so
-        // those keep the shared form.
+        // split + merge 25.9 vs 26.9 us; on the multi-round grids of four heads it was 7-8% slower
+        // (the shared staging reads 512 contiguous bytes of each row per instruction), so those keep
+        // the shared form.
         __bf16* pk = reinterpret_cast<__bf16*>(&k_lds[0][0][0][0]) + wave_all * (2 * 16 * kHeadDim);
         __bf16* pv = pk + 16 * kHeadDim;
         static_assert(sizeof(k_lds) >= sizeof(__bf16) * kWaves * 2 * 16 * kHeadDim, "private regions");
@@ -447,26 +447,20 @@ __global__ __launch_bounds__(kSplitThreads * kHeads) void decode_split_bf16_kern
             fold_key_ops(m, dsum, acc, ops, q_op, static_cast<int>(base0) + kBlockKeys * i, tail_from, lim, c2, grp,
                          tile);
         };
-        // Two blocks in flight during each fold; the scheduling barriers keep each half's loads
-        // ahead of its fold (with no s_barrier in the loop the compiler would otherwise gather them
-        // and wait for all of them at once).
-        KvStage ra, rb;
+        // One block in flight during each fold (the loads of block i + 1, issued before it): with two
+        // the split took 24.4-24.7 us instead of 23.4-23.6 on 8 x 8192 keys, as a plain read of the
+        // same pattern is faster with 32 KB than with 64 KB in flight per compute unit. The
+        // scheduling barriers keep the loads ahead of the fold (with no s_barrier in the loop the
+        // compiler would otherwise move them).
+        KvStage ra;
         pload(ra, 0);
         pstore(ra);
-        pload(ra, 1);
-        for (int i = 0; i < blocks;) {
-            pload(rb, i + 2);
+        for (int i = 0; i < blocks; ++i) {
+            pload(ra, i + 1);
             __builtin_amdgcn_sched_barrier(0);
             pfold(i);
             pstore(ra);
             __builtin_amdgcn_sched_barrier(0);
-            if (++i >= blocks) break;
-            pload(ra, i + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            pfold(i);
-            pstore(rb);
-            __builtin_amdgcn_sched_barrier(0);
-            ++i;
         }
         // Every wave is done with its private region before the tiles are reused below.
         __syncthreads();

@@ -225,6 +225,23 @@ def measure_ceilings(torch, dev):
         best = max(best, (lib.sinkattn_ceiling_mfma_bf16_flop(blocks, 4000) / (ms * 1e-3) / 1e12, blocks))
     res["mfma_bf16_loop_tflops"] = round(best[0], 1)
     res["mfma_bf16_loop_blocks"] = best[1]
+    lib.sinkattn_ceiling_mfma_bf16_random.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sinkattn_ceiling_mfma_bf16_random_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sinkattn_ceiling_mfma_bf16_random_flop.restype = ctypes.c_double
+
+    def mfma_random(blocks, iters):
+        stream_ptr = torch.cuda.current_stream().cuda_stream
+        rc = lib.sinkattn_ceiling_mfma_bf16_random(blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                                   ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"random-operand MFMA ceiling launch failed ({rc})")
+
+    best = (0.0, 0)
+    for blocks in (512, 1024):
+        ms = _time_graph(_capture(lambda i, b=blocks: mfma_random(b, 2000), 3, torch), 3, torch, replays=5)
+        best = max(best, (lib.sinkattn_ceiling_mfma_bf16_random_flop(blocks, 2000) / (ms * 1e-3) / 1e12, blocks))
+    res["mfma_bf16_random_loop_tflops"] = round(best[0], 1)
+    res["mfma_bf16_random_loop_blocks"] = best[1]
     res["issue_cycles"] = measure_issue_cycles(lib, torch, dev, sink)
     n = 8192
     gen = torch.Generator().manual_seed(1010)
@@ -602,7 +619,11 @@ def main():
                          "algorithmic_flop_per_launch": flops,
                          "measured_mfma_loop_tflops": ceilings["mfma_bf16_loop_tflops"] if ceilings else None,
                          "frac_of_measured_mfma_loop": (round(tflops / ceilings["mfma_bf16_loop_tflops"], 4)
-                                                        if ceilings else None)},
+                                                        if ceilings else None),
+                         "measured_mfma_random_loop_tflops": (ceilings["mfma_bf16_random_loop_tflops"]
+                                                              if ceilings else None),
+                         "frac_of_measured_mfma_random_loop": (
+                             round(tflops / ceilings["mfma_bf16_random_loop_tflops"], 4) if ceilings else None)},
         }
 
     # ---------------------------------------------------------------- split-KV (append) prefill

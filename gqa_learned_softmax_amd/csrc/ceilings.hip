@@ -90,6 +90,42 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* out) {
     if (s == -1.0f) out[0] = s;  // never true for these operands (every product is >= 0)
 }
 
+// The same MFMA loop on operands that look like real data: four A and four B operands per lane of
+// uniform random bf16 values in [-2, 2) (full mantissas, from a per-thread xorshift), cycled so that
+// consecutive MFMAs never share an operand. The chip's clock under MFMA work depends on how many
+// operand bits switch, so this rate is the one a kernel multiplying random bf16 data can approach.
+// Eight MFMAs per iteration (four chains of two).
+__global__ __launch_bounds__(256) void mfma_random_kernel(int iters, float* out) {
+    uint32_t h = (blockIdx.x * 256u + threadIdx.x) * 0x9E3779B9u + 0x7F4A7C15u;
+    auto next = [&]() {
+        h ^= h << 13;
+        h ^= h >> 17;
+        h ^= h << 5;
+        return static_cast<__bf16>(static_cast<float>(static_cast<int>(h & 0xFFFFu) - 32768) * (1.0f / 16384.0f));
+    };
+    bf16x8 a0, a1, a2, a3, b0, b1, b2, b3;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a0[e] = next(); a1[e] = next(); a2[e] = next(); a3[e] = next();
+        b0[e] = next(); b1[e] = next(); b2[e] = next(); b3[e] = next();
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b2, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b3, c3, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b2, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b3, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b0, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, c3, 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    if (s == 1234567.0f) out[0] = s;  // keeps the products live; the value is never this
+}
+
 // Issue-cost loops: each wave repeats one fixed group of instructions on eight rotating fp32
 // registers and independent accumulators, so (kinds 0-6) nothing waits on a recent result and the
 // time per group is what the instructions themselves cost the SIMD; kind 7 chains each multiply
@@ -211,6 +247,18 @@ int sinkattn_ceiling_mfma_bf16(int blocks, int iters, void* out4, void* stream) 
     mfma_loop_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
         iters, static_cast<float*>(out4));
     return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int sinkattn_ceiling_mfma_bf16_random(int blocks, int iters, void* out4, void* stream) {
+    if (out4 == nullptr || blocks <= 0 || iters <= 0) return 1;
+    mfma_random_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        iters, static_cast<float*>(out4));
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+double sinkattn_ceiling_mfma_bf16_random_flop(int blocks, int iters) {
+    // 4 waves per block, 8 MFMAs per iteration, 32 x 32 x 16 x 2 flop each.
+    return static_cast<double>(blocks) * 4.0 * iters * 8.0 * 32.0 * 32.0 * 16.0 * 2.0;
 }
 
 double sinkattn_ceiling_mfma_bf16_flop(int blocks, int iters) {

@@ -41,6 +41,14 @@ int sinkattn_ceiling_mfma_bf16(int blocks, int iters, void* out4, void* stream);
 /* Floating-point operations of one sinkattn_ceiling_mfma_bf16(blocks, iters) launch. */
 double sinkattn_ceiling_mfma_bf16_flop(int blocks, int iters);
 
+/* As sinkattn_ceiling_mfma_bf16, on random bf16 operands (four A and four B per lane, uniform in
+ * [-2, 2), cycled so consecutive MFMAs share none), 8 MFMAs per wave and iteration: the MFMA rate at
+ * the clock the chip holds when the operand bits switch as real data's do. */
+int sinkattn_ceiling_mfma_bf16_random(int blocks, int iters, void* out4, void* stream);
+
+/* Floating-point operations of one sinkattn_ceiling_mfma_bf16_random(blocks, iters) launch. */
+double sinkattn_ceiling_mfma_bf16_random_flop(int blocks, int iters);
+
 /* `blocks` work-groups of four waves, each wave repeating `iters` times one group of instructions
  * (independent of recent results except in kind 7), by `kind`: 0: 16 v_exp_f32; 1: 16 v_mul_f32;
  * 2: 16 v_cvt_pk_bf16_f32; 3: 16 v_fma_f32; 4: 4 v_mfma_f32_32x32x16_bf16; 5: 4

@@ -69,7 +69,8 @@ def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
     text = open(CEILINGS_HEADER).read()
     names = set(re.findall(r"^\s*(?:int|double)\s+(sinkattn_ceiling_\w+)\s*\(", text, flags=re.M))
     assert names == {"sinkattn_ceiling_stream_read", "sinkattn_ceiling_stream_read_slices", "sinkattn_ceiling_mfma_bf16",
-                     "sinkattn_ceiling_mfma_bf16_flop", "sinkattn_ceiling_issue"}
+                     "sinkattn_ceiling_mfma_bf16_flop", "sinkattn_ceiling_mfma_bf16_random",
+                     "sinkattn_ceiling_mfma_bf16_random_flop", "sinkattn_ceiling_issue"}
     lib = ctypes.CDLL(CEILINGS_LIB)
     for name in names:
         assert hasattr(lib, name), name
@@ -103,6 +104,13 @@ def test_ceilings_library_exports_its_header_and_rejects_bad_arguments():
     assert lib.sinkattn_ceiling_issue(0, 8, 10, None, fake, None) == 1
     # 4 waves x 4 MFMAs of 32 x 32 x 16 x 2 flop per block and iteration.
     assert lib.sinkattn_ceiling_mfma_bf16_flop(3, 5) == 3 * 5 * 4 * 4 * 32 * 32 * 16 * 2
+    lib.sinkattn_ceiling_mfma_bf16_random.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sinkattn_ceiling_mfma_bf16_random_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.sinkattn_ceiling_mfma_bf16_random_flop.restype = ctypes.c_double
+    assert lib.sinkattn_ceiling_mfma_bf16_random(0, 10, fake, None) == 1
+    assert lib.sinkattn_ceiling_mfma_bf16_random(8, 0, fake, None) == 1
+    assert lib.sinkattn_ceiling_mfma_bf16_random(8, 10, None, None) == 1
+    assert lib.sinkattn_ceiling_mfma_bf16_random_flop(3, 5) == 3 * 5 * 4 * 8 * 32 * 32 * 16 * 2
 
 
 def test_version_and_status_strings():

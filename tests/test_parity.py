@@ -754,6 +754,8 @@ MULTI_CASES = [
     ("t3_odd_kv_heads", [300, 77], 320, 4, 12, 3, 3),
     ("t2_paired_heads", [250, 3, 0, 129], 256, 16, 64, 8, 2),         # paired-head work-groups
     ("t4_paired_heads", [250, 3, 0, 129], 256, 16, 64, 8, 4),
+    # 8 x 4 x 8 = 256 paired work-groups: one round, private staging, lengths at and below T
+    ("t2_private_ragged", [8191, 1, 0, 2, 4097, 65, 64, 6000], 8192, 8, 64, 8, 2),
     ("t2_quad_heads", [4 + (37 * i) % 509 for i in range(32)], 512, 8, 64, 8, 2),   # four-head work-groups
     ("t4_quad_heads", [4 + (37 * i) % 509 for i in range(32)], 512, 8, 64, 8, 4),
     ("t1_is_decode", [700, 5], 768, 4, 64, 8, 1),
@@ -787,7 +789,8 @@ def test_decode_multi_bf16(name, lens, cap, chunks, hq, hkv, t):
 @pytest.mark.parametrize("name,lens,cap,chunks,hq,hkv,t",
                          [c for c in MULTI_CASES if c[0] in ("t3_partial_tile", "t4_ragged_short", "t8_four_tiles",
                                                              "t4_paired_heads", "t2_quad_heads", "t4_quad_heads",
-                                                             "t6_group2", "t4_many_chunks_one_round")],
+                                                             "t6_group2", "t4_many_chunks_one_round",
+                                                             "t2_private_ragged")],
                          ids=lambda x: x if isinstance(x, str) else None)
 def test_decode_multi_fused_bf16(name, lens, cap, chunks, hq, hkv, t):
     sa = _sa()
